@@ -1,0 +1,10 @@
+"""MI355X-native blockwise ring attention (one GPU's share of context parallelism).
+
+The computation lives in ``libra.so`` (HIP kernels for gfx950 behind the C ABI of
+``include/ra.h``); this package only marshals torch tensors into that ABI.
+"""
+from .ops import (Chunks, bwd_chunk, bwd_delta, fwd_chunk, head_to_seq, merge_lse, ring_bwd, ring_fwd,
+                  ring_order, rows_desc, seq_head_permute, seq_to_head, split_sizes, tensor_desc)
+
+__all__ = ["Chunks", "bwd_chunk", "bwd_delta", "fwd_chunk", "head_to_seq", "merge_lse", "ring_bwd", "ring_fwd",
+           "ring_order", "rows_desc", "seq_head_permute", "seq_to_head", "split_sizes", "tensor_desc"]

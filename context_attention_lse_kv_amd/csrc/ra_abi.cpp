@@ -1,0 +1,465 @@
+// C ABI of the ring-attention library: host-side validation (before any
+// launch), chunk-table and ring-order handling, workspace carving and the
+// launch sequence of the ring sweeps.  Everything is enqueued on the caller's
+// stream; nothing here allocates device memory.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ra_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+ra_status ok() {
+    g_err.clear();
+    return RA_OK;
+}
+
+#define RA_TRY(expr)                      \
+    do {                                  \
+        const ra_status _st = (expr);     \
+        if (_st != RA_OK) return _st;     \
+    } while (0)
+
+#define RA_HIP(expr)                                                                  \
+    do {                                                                              \
+        const hipError_t _e = (expr);                                                 \
+        if (_e != hipSuccess) return fail(RA_E_HIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+    } while (0)
+
+size_t esize(int32_t dt) { return dt == RA_BF16 ? 2 : dt == RA_F32 ? 4 : 0; }
+const char* dname(int32_t dt) { return dt == RA_BF16 ? "bf16" : dt == RA_F32 ? "fp32" : "invalid"; }
+
+int64_t numel(const ra_tensor& t) { return (int64_t)t.B * t.S * t.H * t.D; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// True if no two logical elements of the tensor share an address.
+bool non_overlapping(const ra_tensor& t) {
+    struct Dim { int64_t stride, extent; };
+    std::vector<Dim> dims = {{1, t.D}, {t.sH, t.H}, {t.sS, t.S}, {t.sB, t.B}};
+    dims.erase(std::remove_if(dims.begin(), dims.end(), [](const Dim& d) { return d.extent <= 1; }), dims.end());
+    std::sort(dims.begin(), dims.end(), [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+    int64_t span = 0;  // largest offset reachable by the inner dims
+    for (const Dim& d : dims) {
+        if (d.stride <= span) return false;
+        span += d.stride * (d.extent - 1);
+    }
+    return true;
+}
+
+// Byte range [lo, hi) that a tensor touches.
+void byte_range(const ra_tensor& t, uintptr_t& lo, uintptr_t& hi) {
+    const size_t es = esize(t.dtype);
+    lo = (uintptr_t)t.data;
+    if (numel(t) == 0) {
+        hi = lo;
+        return;
+    }
+    const int64_t last = (int64_t)(t.B - 1) * t.sB + (int64_t)(t.S - 1) * t.sS + (int64_t)(t.H - 1) * t.sH + (t.D - 1);
+    hi = lo + (uintptr_t)((last + 1) * es);
+}
+
+ra_status check_tensor(const ra_tensor* t, const char* name, bool any_d = false) {
+    if (!t) return fail(RA_E_ARG, "%s: descriptor is NULL", name);
+    const size_t es = esize(t->dtype);
+    if (es == 0) return fail(RA_E_DTYPE, "%s: dtype %d is neither RA_BF16 nor RA_F32", name, t->dtype);
+    if (t->B < 1 || t->H < 1 || t->D < 1 || t->S < 0)
+        return fail(RA_E_SHAPE, "%s: need B, H, D >= 1 and S >= 0 (got B=%d S=%d H=%d D=%d)", name, t->B, t->S,
+                    t->H, t->D);
+    if (!any_d && t->D != 64 && t->D != 128)
+        return fail(RA_E_UNSUPPORTED, "%s: head dim D=%d is not built (D must be 64 or 128)", name, t->D);
+    if (any_d && (t->D * es) % 16 != 0)
+        return fail(RA_E_ALIGN, "%s: a row of D=%d %s elements is not a multiple of 16 bytes", name, t->D,
+                    dname(t->dtype));
+    if (t->sB < 0 || t->sS < 0 || t->sH < 0) return fail(RA_E_ARG, "%s: negative stride", name);
+    if (numel(*t) > 0 && !t->data) return fail(RA_E_ARG, "%s: data is NULL", name);
+    if ((uintptr_t)t->data % 16) return fail(RA_E_ALIGN, "%s: data pointer is not 16-byte aligned", name);
+    if ((t->sB * es) % 16 || (t->sS * es) % 16 || (t->sH * es) % 16)
+        return fail(RA_E_ALIGN, "%s: strides (%lld, %lld, %lld) elements are not multiples of 16 bytes", name,
+                    (long long)t->sB, (long long)t->sS, (long long)t->sH);
+    if (!non_overlapping(*t)) return fail(RA_E_ARG, "%s: strides make elements overlap", name);
+    return RA_OK;
+}
+
+ra_status check_rows(const ra_lse* l, const char* name, int32_t B, int32_t H, int32_t S) {
+    if (!l) return fail(RA_E_ARG, "%s: descriptor is NULL", name);
+    if (l->B != B || l->H != H || l->S != S)
+        return fail(RA_E_SHAPE, "%s: shape [%d,%d,%d] does not match [B,H,S]=[%d,%d,%d]", name, l->B, l->H, l->S, B,
+                    H, S);
+    if (l->sB < 0 || l->sH < 0) return fail(RA_E_ARG, "%s: negative stride", name);
+    if ((int64_t)B * H * S > 0 && !l->data) return fail(RA_E_ARG, "%s: data is NULL", name);
+    if ((uintptr_t)l->data % 4) return fail(RA_E_ALIGN, "%s: data pointer is not 4-byte aligned", name);
+    if (S > 1 || H > 1 || B > 1) {
+        // rows of the statistic must not overlap: sH >= S (when H > 1) and sB >= (H-1)*sH + S (when B > 1)
+        if (H > 1 && l->sH < S) return fail(RA_E_ARG, "%s: sH < S makes rows overlap", name);
+        if (B > 1 && l->sB < (int64_t)(H - 1) * l->sH + S) return fail(RA_E_ARG, "%s: sB makes rows overlap", name);
+    }
+    return RA_OK;
+}
+
+bool same_shape(const ra_tensor& a, const ra_tensor& b) { return a.B == b.B && a.S == b.S && a.H == b.H && a.D == b.D; }
+
+ra_status check_scale(float scale) {
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(RA_E_ARG, "scale must be finite and > 0 (got %g)", scale);
+    return RA_OK;
+}
+
+// q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] with matching dtype, batch and head dim, Hkv | Hq.
+ra_status check_qkv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v) {
+    RA_TRY(check_tensor(q, "q"));
+    RA_TRY(check_tensor(k, "k"));
+    RA_TRY(check_tensor(v, "v"));
+    if (q->dtype != k->dtype || q->dtype != v->dtype)
+        return fail(RA_E_DTYPE, "q, k, v must share one dtype (got %s, %s, %s)", dname(q->dtype), dname(k->dtype),
+                    dname(v->dtype));
+    if (k->B != q->B || v->B != q->B) return fail(RA_E_SHAPE, "batch of q, k, v differs");
+    if (k->D != q->D || v->D != q->D) return fail(RA_E_SHAPE, "head dim of q, k, v differs");
+    if (k->S != v->S || k->H != v->H) return fail(RA_E_SHAPE, "k and v must have the same sequence length and heads");
+    if (q->H % k->H != 0)
+        return fail(RA_E_SHAPE,
+                    "Number of heads in key/value must divide number of heads in query (H_q=%d, H_kv=%d)", q->H, k->H);
+    return RA_OK;
+}
+
+ra_status check_acc(const ra_tensor* t, const char* name, const ra_tensor& like) {
+    RA_TRY(check_tensor(t, name));
+    if (t->dtype != RA_F32) return fail(RA_E_DTYPE, "%s: accumulator must be fp32", name);
+    if (!same_shape(*t, like)) return fail(RA_E_SHAPE, "%s: shape does not match", name);
+    return RA_OK;
+}
+
+ra_status check_chunks(const ra_chunks* c, int32_t Sk) {
+    if (!c) return fail(RA_E_ARG, "chunks: descriptor is NULL");
+    if (c->n < 1 || c->n > 65536) return fail(RA_E_ARG, "chunks: n=%d out of range [1, 65536]", c->n);
+    if (!c->start || !c->len || !c->order) return fail(RA_E_ARG, "chunks: start/len/order must not be NULL");
+    std::vector<int> seen(c->n, 0);
+    for (int i = 0; i < c->n; ++i) {
+        const int o = c->order[i];
+        if (o < 0 || o >= c->n || seen[o]++) return fail(RA_E_ARG, "chunks: order is not a permutation of 0..n-1");
+    }
+    std::vector<std::pair<int64_t, int64_t>> iv;
+    for (int i = 0; i < c->n; ++i) {
+        if (c->len[i] < 0 || c->start[i] < 0) return fail(RA_E_ARG, "chunks: negative start or length");
+        if ((int64_t)c->start[i] + c->len[i] > Sk)
+            return fail(RA_E_SHAPE, "chunks: chunk %d [%d, %d) runs past S_k=%d", i, c->start[i],
+                        c->start[i] + c->len[i], Sk);
+        if (c->len[i] > 0) iv.push_back({c->start[i], c->len[i]});
+    }
+    std::sort(iv.begin(), iv.end());
+    int64_t at = 0;
+    for (auto& x : iv) {
+        if (x.first != at) return fail(RA_E_SHAPE, "chunks do not tile [0, S_k) exactly (gap or overlap at %lld)", (long long)at);
+        at += x.second;
+    }
+    if (at != Sk) return fail(RA_E_SHAPE, "chunks cover %lld of S_k=%d rows", (long long)at, Sk);
+    return RA_OK;
+}
+
+ra_tensor seq_slice(const ra_tensor& t, int32_t start, int32_t len) {
+    ra_tensor r = t;
+    r.data = (char*)t.data + (int64_t)start * t.sS * (int64_t)esize(t.dtype);
+    r.S = len;
+    return r;
+}
+
+ra_tensor contiguous_f32(void* data, const ra_tensor& like) {
+    ra_tensor r;
+    r.data = data;
+    r.dtype = RA_F32;
+    r.B = like.B; r.S = like.S; r.H = like.H; r.D = like.D;
+    r.sH = like.D;
+    r.sS = (int64_t)like.H * like.D;
+    r.sB = (int64_t)like.S * like.H * like.D;
+    return r;
+}
+
+ra_lse contiguous_rows(void* data, int32_t B, int32_t H, int32_t S) {
+    ra_lse r;
+    r.data = (float*)data;
+    r.B = B; r.H = H; r.S = S;
+    r.sH = S;
+    r.sB = (int64_t)H * S;
+    return r;
+}
+
+ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
+                            const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+    if (k.S == 0) {
+        if (!merge) {  // the partial of an empty chunk is the merge identity
+            RA_HIP(ra::launch_zero_f32(out, s));
+            RA_HIP(ra::launch_fill_rows(lse, -INFINITY, s));
+        }
+        return RA_OK;
+    }
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_fwd_chunk_bf16(q, k, v, scale, out, lse, merge, s));
+    else RA_HIP(ra::launch_fwd_chunk_f32(q, k, v, scale, out, lse, merge, s));
+    return RA_OK;
+}
+
+ra_status enqueue_bwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                            const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq,
+                            const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_chunk_bf16(q, k, v, dout, lse, delta, scale, dq, dk, dv, s));
+    else RA_HIP(ra::launch_bwd_chunk_f32(q, k, v, dout, lse, delta, scale, dq, dk, dv, s));
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_fwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, float scale, ra_tensor* out,
+                       ra_lse* lse, int32_t merge, void* stream) {
+    RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_acc(out, "out", *q));
+    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
+    RA_TRY(check_scale(scale));
+    if (merge != 0 && merge != 1) return fail(RA_E_ARG, "merge must be 0 or 1");
+    RA_TRY(enqueue_fwd_chunk(*q, *k, *v, scale, *out, *lse, merge, (hipStream_t)stream));
+    return ok();
+}
+
+ra_status ra_merge_lse(ra_tensor* out_acc, ra_lse* lse_acc, const ra_tensor* out_part, const ra_lse* lse_part,
+                       void* stream) {
+    RA_TRY(check_tensor(out_acc, "out_acc"));
+    RA_TRY(check_acc(out_part, "out_part", *out_acc));
+    if (out_acc->dtype != RA_F32) return fail(RA_E_DTYPE, "out_acc must be fp32");
+    RA_TRY(check_rows(lse_acc, "lse_acc", out_acc->B, out_acc->H, out_acc->S));
+    RA_TRY(check_rows(lse_part, "lse_part", out_acc->B, out_acc->H, out_acc->S));
+    RA_HIP(ra::launch_merge_lse(*out_acc, *lse_acc, *out_part, *lse_part, (hipStream_t)stream));
+    return ok();
+}
+
+ra_status ra_bwd_delta(const ra_tensor* out, const ra_tensor* dout, ra_lse* delta, void* stream) {
+    RA_TRY(check_tensor(out, "out"));
+    RA_TRY(check_tensor(dout, "dout"));
+    if (!same_shape(*out, *dout)) return fail(RA_E_SHAPE, "out and dout must have the same shape");
+    if (out->dtype == RA_BF16 && dout->dtype == RA_F32)
+        return fail(RA_E_DTYPE, "bf16 out with fp32 dout is not supported");
+    RA_TRY(check_rows(delta, "delta", out->B, out->H, out->S));
+    RA_HIP(ra::launch_bwd_delta(*out, *dout, *delta, (hipStream_t)stream));
+    return ok();
+}
+
+ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                       const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, ra_tensor* dk_acc,
+                       ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+    RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_tensor(dout, "dout"));
+    if (dout->dtype != q->dtype || !same_shape(*dout, *q)) return fail(RA_E_SHAPE, "dout must match q in shape and dtype");
+    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
+    RA_TRY(check_rows(delta, "delta", q->B, q->H, q->S));
+    RA_TRY(check_scale(scale));
+    RA_TRY(check_acc(dq_acc, "dq_acc", *q));
+    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
+    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
+    if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate) {
+        RA_HIP(ra::launch_zero_f32(*dk_acc, s));
+        RA_HIP(ra::launch_zero_f32(*dv_acc, s));
+    }
+    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_chunk(*q, *k, *v, *dout, *lse, *delta, scale, *dq_acc, *dk_acc, *dv_acc, s));
+    return ok();
+}
+
+size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
+    if (!q || !out || out->dtype != RA_BF16) return 0;
+    return round256((size_t)numel(*q) * 4);
+}
+
+size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq, const ra_tensor* dk,
+                                   const ra_tensor* dv) {
+    if (!q || !k) return 0;
+    size_t n = round256((size_t)q->B * q->H * q->S * 4);
+    if (dq && dq->dtype == RA_BF16) n += round256((size_t)numel(*q) * 4);
+    if (dk && dk->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
+    if (dv && dv->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
+    return n;
+}
+
+static ra_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return RA_OK;
+    if (!ws) return fail(RA_E_WORKSPACE, "workspace of %zu bytes needed, got NULL", need);
+    if ((uintptr_t)ws % 256) return fail(RA_E_ALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(RA_E_WORKSPACE, "workspace of %zu bytes needed, got %zu", need, ws_bytes);
+    return RA_OK;
+}
+
+ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_chunks* chunks, float scale,
+                      ra_tensor* out, ra_lse* lse, void* ws, size_t ws_bytes, void* stream) {
+    RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_tensor(out, "out"));
+    if (!same_shape(*out, *q)) return fail(RA_E_SHAPE, "out must have the shape of q");
+    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
+    RA_TRY(check_scale(scale));
+    RA_TRY(check_chunks(chunks, k->S));
+    const size_t need = ra_ring_fwd_workspace_bytes(q, out);
+    RA_TRY(check_ws(ws, ws_bytes, need));
+    hipStream_t s = (hipStream_t)stream;
+    const ra_tensor acc = out->dtype == RA_F32 ? *out : contiguous_f32(ws, *q);
+    for (int i = 0; i < chunks->n; ++i) {
+        const int c = chunks->order[i];
+        const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);
+        const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
+        RA_TRY(enqueue_fwd_chunk(*q, kc, vc, scale, acc, *lse, i > 0 ? 1 : 0, s));
+    }
+    if (out->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(acc, *out, s));
+    return ok();
+}
+
+ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
+                      const ra_tensor* dout, const ra_lse* lse, const ra_chunks* chunks, float scale, ra_tensor* dq,
+                      ra_tensor* dk, ra_tensor* dv, void* ws, size_t ws_bytes, void* stream) {
+    RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_tensor(out, "out"));
+    RA_TRY(check_tensor(dout, "dout"));
+    if (!same_shape(*out, *q) || !same_shape(*dout, *q)) return fail(RA_E_SHAPE, "out and dout must have the shape of q");
+    if (dout->dtype != q->dtype) return fail(RA_E_DTYPE, "dout must have the dtype of q");
+    if (out->dtype == RA_BF16 && dout->dtype == RA_F32) return fail(RA_E_DTYPE, "bf16 out with fp32 dout is not supported");
+    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
+    RA_TRY(check_scale(scale));
+    RA_TRY(check_chunks(chunks, k->S));
+    RA_TRY(check_tensor(dq, "dq"));
+    RA_TRY(check_tensor(dk, "dk"));
+    RA_TRY(check_tensor(dv, "dv"));
+    if (!same_shape(*dq, *q) || !same_shape(*dk, *k) || !same_shape(*dv, *v))
+        return fail(RA_E_SHAPE, "dq, dk, dv must have the shapes of q, k, v");
+    const size_t need = ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv);
+    RA_TRY(check_ws(ws, ws_bytes, need));
+    hipStream_t s = (hipStream_t)stream;
+    char* p = (char*)ws;
+    const ra_lse delta = contiguous_rows(p, q->B, q->H, q->S);
+    p += round256((size_t)q->B * q->H * q->S * 4);
+    ra_tensor dq_acc = *dq, dk_acc = *dk, dv_acc = *dv;
+    if (dq->dtype == RA_BF16) { dq_acc = contiguous_f32(p, *q); p += round256((size_t)numel(*q) * 4); }
+    if (dk->dtype == RA_BF16) { dk_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
+    if (dv->dtype == RA_BF16) { dv_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
+
+    RA_HIP(ra::launch_bwd_delta(*out, *dout, delta, s));
+    RA_HIP(ra::launch_zero_f32(dq_acc, s));
+    RA_HIP(ra::launch_zero_f32(dk_acc, s));
+    RA_HIP(ra::launch_zero_f32(dv_acc, s));
+    for (int i = 0; i < chunks->n; ++i) {
+        const int c = chunks->order[i];
+        if (chunks->len[c] == 0 || q->S == 0) continue;
+        const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);
+        const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
+        const ra_tensor dkc = seq_slice(dk_acc, chunks->start[c], chunks->len[c]);
+        const ra_tensor dvc = seq_slice(dv_acc, chunks->start[c], chunks->len[c]);
+        RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, scale, dq_acc, dkc, dvc, s));
+    }
+    if (dq->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));
+    if (dk->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dk_acc, *dk, s));
+    if (dv->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dv_acc, *dv, s));
+    return ok();
+}
+
+ra_status ra_seq_head_permute(const ra_tensor* in, int32_t n_in, ra_tensor* out, int32_t n_out, int32_t dir,
+                              void* stream) {
+    if (dir != 0 && dir != 1) return fail(RA_E_ARG, "dir must be 0 (seq->head) or 1 (head->seq)");
+    if (!in || !out) return fail(RA_E_ARG, "in/out arrays must not be NULL");
+    if (n_in < 1 || n_in > ra::kMaxRanks || n_out != n_in)
+        return fail(RA_E_ARG, "need 1 <= R <= %d ranks and as many outputs as inputs (got %d, %d)", ra::kMaxRanks, n_in,
+                    n_out);
+    const int R = n_in;
+    for (int i = 0; i < R; ++i) {
+        char nm[32];
+        snprintf(nm, sizeof nm, "in[%d]", i);
+        RA_TRY(check_tensor(&in[i], nm, true));
+        snprintf(nm, sizeof nm, "out[%d]", i);
+        RA_TRY(check_tensor(&out[i], nm, true));
+        if (in[i].dtype != in[0].dtype || out[i].dtype != in[0].dtype)
+            return fail(RA_E_DTYPE, "all exchange tensors must share one dtype");
+        if (in[i].B != in[0].B || out[i].B != in[0].B || in[i].D != in[0].D || out[i].D != in[0].D)
+            return fail(RA_E_SHAPE, "batch and head dim must agree across exchange tensors");
+    }
+    ra::PermuteTable tab;
+    memset(&tab, 0, sizeof tab);
+    tab.n_in = R;
+    tab.n_out = R;
+    tab.dir = dir;
+    tab.elem_bytes = (int32_t)esize(in[0].dtype);
+    // seq-side tensors (shards, all heads) and head-side tensors (head groups, whole sequence)
+    const ra_tensor* seqside = dir == 0 ? in : out;
+    const ra_tensor* headside = dir == 0 ? out : in;
+    const int32_t H = seqside[0].H;
+    const int32_t S = headside[0].S;
+    tab.off[0] = 0;
+    tab.hoff[0] = 0;
+    for (int i = 0; i < R; ++i) {
+        if (seqside[i].H != H) return fail(RA_E_SHAPE, "every sequence shard must hold all H=%d heads", H);
+        if (headside[i].S != S) return fail(RA_E_SHAPE, "every head group must hold the whole sequence S=%d", S);
+        tab.off[i + 1] = tab.off[i] + seqside[i].S;
+        tab.hoff[i + 1] = tab.hoff[i] + headside[i].H;
+    }
+    if (tab.off[R] != S) return fail(RA_E_SHAPE, "shard lengths sum to %d, head groups hold S=%d", tab.off[R], S);
+    if (tab.hoff[R] != H) return fail(RA_E_SHAPE, "head groups sum to %d heads, shards hold H=%d", tab.hoff[R], H);
+    for (int i = 0; i < R; ++i)
+        for (int j = 0; j < R; ++j) {
+            uintptr_t a0, a1, b0, b1;
+            byte_range(in[i], a0, a1);
+            byte_range(out[j], b0, b1);
+            if (a0 < b1 && b0 < a1) return fail(RA_E_ARG, "in[%d] and out[%d] overlap in memory", i, j);
+        }
+    for (int i = 0; i < R; ++i) {
+        tab.in[i] = in[i];
+        tab.out[i] = out[i];
+    }
+    RA_HIP(ra::launch_permute(tab, (hipStream_t)stream));
+    return ok();
+}
+
+ra_status ra_split_sizes(int32_t n, int32_t parts, int32_t* sizes) {
+    if (!sizes) return fail(RA_E_ARG, "sizes must not be NULL");
+    if (parts < 1 || n < 0) return fail(RA_E_ARG, "need parts >= 1 and n >= 0");
+    const int32_t base = n / parts, extra = n % parts;
+    for (int32_t i = 0; i < parts; ++i) sizes[i] = base + (i < extra ? 1 : 0);
+    return ok();
+}
+
+ra_status ra_ring_order(int32_t R, int32_t rank, int32_t* order) {
+    if (!order) return fail(RA_E_ARG, "order must not be NULL");
+    if (R < 1 || rank < 0 || rank >= R) return fail(RA_E_ARG, "need R >= 1 and 0 <= rank < R");
+    for (int32_t i = 0; i < R; ++i) order[i] = ((rank - i) % R + R) % R;
+    return ok();
+}
+
+const char* ra_status_string(ra_status s) {
+    switch (s) {
+        case RA_OK: return "RA_OK";
+        case RA_E_ARG: return "RA_E_ARG";
+        case RA_E_SHAPE: return "RA_E_SHAPE";
+        case RA_E_DTYPE: return "RA_E_DTYPE";
+        case RA_E_ALIGN: return "RA_E_ALIGN";
+        case RA_E_UNSUPPORTED: return "RA_E_UNSUPPORTED";
+        case RA_E_WORKSPACE: return "RA_E_WORKSPACE";
+        case RA_E_HIP: return "RA_E_HIP";
+    }
+    return "RA_E_UNKNOWN";
+}
+
+const char* ra_last_error(void) { return g_err.c_str(); }
+
+const char* ra_version(void) { return "ra 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (ra_abi.cpp) and the kernel
+// launchers (*.hip).  Descriptors are passed to kernels by value.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/ra.h"
+
+namespace ra {
+
+// Tile geometry of the bf16 MFMA kernels (also used by host-side sizing).
+constexpr int kFwdRowsPerWave = 32;
+constexpr int kFwdWaves = 4;
+constexpr int kFwdBlockM = kFwdRowsPerWave * kFwdWaves;  // query rows per workgroup
+constexpr int kFwdBlockN = 64;                            // keys per LDS tile
+constexpr int kBwdKeysPerWave = 32;
+constexpr int kBwdWaves = 4;
+constexpr int kBwdBlockN = kBwdKeysPerWave * kBwdWaves;  // keys per workgroup
+constexpr int kBwdBlockM = 64;                            // query rows per LDS tile
+
+constexpr int kMaxRanks = 16;  // exchange fan-out limit (kernel argument table)
+
+struct PermuteTable {
+    int32_t n_in, n_out, dir, elem_bytes;
+    ra_tensor in[kMaxRanks];
+    ra_tensor out[kMaxRanks];
+    int32_t off[kMaxRanks + 1];  // seq offsets (dir 0: of inputs; dir 1: of outputs)
+    int32_t hoff[kMaxRanks + 1]; // head offsets (dir 0: of outputs; dir 1: of inputs)
+};
+
+// All launchers enqueue on `s` and return hipGetLastError() of the launch.
+// Shapes have been validated by the caller.
+hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
+                                 const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
+hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
+                                const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
+// Adds this chunk's contribution to dq_acc, dk_acc, dv_acc (all fp32).
+hipError_t launch_bwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
+                                 const ra_tensor& dout, const ra_lse& lse, const ra_lse& delta, float scale,
+                                 const ra_tensor& dq_acc, const ra_tensor& dk_acc, const ra_tensor& dv_acc,
+                                 hipStream_t s);
+hipError_t launch_bwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
+                                const ra_tensor& dout, const ra_lse& lse, const ra_lse& delta, float scale,
+                                const ra_tensor& dq_acc, const ra_tensor& dk_acc, const ra_tensor& dv_acc,
+                                hipStream_t s);
+hipError_t launch_merge_lse(const ra_tensor& out_acc, const ra_lse& lse_acc, const ra_tensor& out_part,
+                            const ra_lse& lse_part, hipStream_t s);
+hipError_t launch_bwd_delta(const ra_tensor& out, const ra_tensor& dout, const ra_lse& delta, hipStream_t s);
+hipError_t launch_cast_f32_to_bf16(const ra_tensor& src, const ra_tensor& dst, hipStream_t s);
+hipError_t launch_zero_f32(const ra_tensor& t, hipStream_t s);
+hipError_t launch_fill_rows(const ra_lse& t, float value, hipStream_t s);
+hipError_t launch_permute(const PermuteTable& tab, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,207 @@
+"""Python binding of the ring-attention library on torch tensors.
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the computation runs in the HIP kernels behind the C ABI
+(include/ra.h).  Layouts are described by strides, never copied: ``layout``
+"bshd" means the tensor is indexed [B, S, H, D], "sbhd" means [S, B, H, D]
+(sequence-first, as in the DeepSpeed DistributedAttention issue's testcase).
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _abi
+from ._abi import RaChunks, RaLse, RaTensor, check, lib
+
+_DT = {torch.bfloat16: _abi.RA_BF16, torch.float32: _abi.RA_F32}
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("ring attention runs on the GPU only: every tensor must be on a HIP device")
+
+
+def tensor_desc(t, layout="bshd"):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor")
+    if t.dtype not in _DT:
+        raise ValueError(f"dtype {t.dtype} not supported (bf16 or fp32)")
+    if t.stride(3) != 1:
+        raise ValueError("the head dim D must be contiguous (stride 1)")
+    if layout == "bshd":
+        B, S, H, D = t.shape
+        sB, sS, sH = t.stride(0), t.stride(1), t.stride(2)
+    elif layout == "sbhd":
+        S, B, H, D = t.shape
+        sB, sS, sH = t.stride(1), t.stride(0), t.stride(2)
+    else:
+        raise ValueError("layout must be 'bshd' or 'sbhd'")
+    return RaTensor(t.data_ptr(), _DT[t.dtype], B, S, H, D, sB, sS, sH)
+
+
+def rows_desc(t):
+    """fp32 [B, H, S] statistic (LSE or delta)."""
+    if t.dim() != 3 or t.dtype != torch.float32 or (t.numel() > 0 and t.stride(2) != 1):
+        raise ValueError("row statistics are fp32 [B, H, S] with S contiguous")
+    return RaLse(t.data_ptr(), t.shape[0], t.shape[1], t.shape[2], t.stride(0), t.stride(1))
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def _arr(xs):
+    return (ctypes.c_int32 * len(xs))(*[int(x) for x in xs])
+
+
+def split_sizes(n, parts):
+    out = (ctypes.c_int32 * parts)()
+    check(lib().ra_split_sizes(n, parts, out), "ra_split_sizes")
+    return list(out)
+
+
+def ring_order(R, rank):
+    out = (ctypes.c_int32 * R)()
+    check(lib().ra_ring_order(R, rank, out), "ra_ring_order")
+    return list(out)
+
+
+class Chunks:
+    """Chunk table: lengths (tiling [0, S_k) in order) and a sweep order."""
+
+    def __init__(self, lens, order=None):
+        lens = [int(x) for x in lens]
+        starts, at = [], 0
+        for n in lens:
+            starts.append(at)
+            at += n
+        self.lens, self.starts = lens, starts
+        self.order = list(range(len(lens))) if order is None else [int(o) for o in order]
+        self._keep = (_arr(starts), _arr(lens), _arr(self.order))
+        self.c = RaChunks(len(lens), *self._keep)
+
+    def __len__(self):
+        return len(self.lens)
+
+
+def fwd_chunk(q, k, v, out, lse, merge, scale=None, layout="bshd"):
+    _dev_check(q, k, v, out, lse)
+    dq, dk, dv, do = (tensor_desc(x, layout) for x in (q, k, v, out))
+    dl = rows_desc(lse)
+    check(lib().ra_fwd_chunk(dq, dk, dv, _scale(scale, q.shape[-1]), do, dl, int(merge), _stream(q)), "ra_fwd_chunk")
+
+
+def merge_lse(out_acc, lse_acc, out_part, lse_part, layout="bshd"):
+    _dev_check(out_acc, lse_acc, out_part, lse_part)
+    check(lib().ra_merge_lse(tensor_desc(out_acc, layout), rows_desc(lse_acc), tensor_desc(out_part, layout),
+                             rows_desc(lse_part), _stream(out_acc)), "ra_merge_lse")
+
+
+def bwd_delta(out, dout, delta, layout="bshd"):
+    _dev_check(out, dout, delta)
+    check(lib().ra_bwd_delta(tensor_desc(out, layout), tensor_desc(dout, layout), rows_desc(delta), _stream(out)),
+          "ra_bwd_delta")
+
+
+def bwd_chunk(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, accumulate, scale=None, layout="bshd"):
+    _dev_check(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc)
+    d = [tensor_desc(x, layout) for x in (q, k, v, dout)]
+    a = [tensor_desc(x, layout) for x in (dq_acc, dk_acc, dv_acc)]
+    check(lib().ra_bwd_chunk(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), _scale(scale, q.shape[-1]),
+                             a[0], a[1], a[2], int(accumulate), _stream(q)), "ra_bwd_chunk")
+
+
+def _rows_shape(q, layout):
+    if layout == "bshd":
+        B, S, H, _ = q.shape
+    else:
+        S, B, H, _ = q.shape
+    return (B, H, S)
+
+
+def ring_fwd(q, k, v, chunks, scale=None, out=None, lse=None, out_dtype=None, layout="bshd", workspace=None):
+    """Sweep the local query shard q over every chunk of (k, v) in ``chunks.order``.
+
+    Returns (out, lse); out has q's layout and ``out_dtype`` (default q.dtype), lse is
+    fp32 [B, H_q, S_q].
+    """
+    _dev_check(q, k, v)
+    if not isinstance(chunks, Chunks):
+        chunks = Chunks(chunks)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(_rows_shape(q, layout), dtype=torch.float32, device=q.device)
+    tq, tk, tv, to = (tensor_desc(x, layout) for x in (q, k, v, out))
+    need = lib().ra_ring_fwd_workspace_bytes(tq, to)
+    ws = _workspace(workspace, need, q.device)
+    check(lib().ra_ring_fwd(tq, tk, tv, ctypes.byref(chunks.c), _scale(scale, q.shape[-1]), to, rows_desc(lse),
+                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), need, _stream(q)), "ra_ring_fwd")
+    return out, lse
+
+
+def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layout="bshd", workspace=None):
+    """Backward sweep in the forward's chunk order; returns (dq, dk, dv)."""
+    _dev_check(q, k, v, out, dout, lse)
+    if not isinstance(chunks, Chunks):
+        chunks = Chunks(chunks)
+    gd = grad_dtype or q.dtype
+    dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    t = [tensor_desc(x, layout) for x in (q, k, v, out, dout, dq, dk, dv)]
+    need = lib().ra_ring_bwd_workspace_bytes(t[0], t[1], t[5], t[6], t[7])
+    ws = _workspace(workspace, need, q.device)
+    check(lib().ra_ring_bwd(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), ctypes.byref(chunks.c),
+                            _scale(scale, q.shape[-1]), t[5], t[6], t[7],
+                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), need, _stream(q)), "ra_ring_bwd")
+    return dq, dk, dv
+
+
+def _workspace(ws, need, device):
+    if need == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace of {need} bytes needed")
+        return ws
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def seq_head_permute(inputs, outputs, direction, layout="bshd"):
+    """Exchange of R simulated ranks (direction 0: seq->head, 1: head->seq) into ``outputs``."""
+    _dev_check(*inputs, *outputs)
+    R = len(inputs)
+    tin = (RaTensor * R)(*[tensor_desc(x, layout) for x in inputs])
+    tout = (RaTensor * len(outputs))(*[tensor_desc(x, layout) for x in outputs])
+    check(lib().ra_seq_head_permute(tin, R, tout, len(outputs), int(direction), _stream(inputs[0])),
+          "ra_seq_head_permute")
+    return outputs
+
+
+def seq_to_head(shards, head_counts, layout="sbhd"):
+    """shards[i]: rank i's sequence shard; returns rank r's head group over the whole sequence."""
+    S = sum(x.shape[0 if layout == "sbhd" else 1] for x in shards)
+    outs = []
+    for h in head_counts:
+        x0 = shards[0]
+        shape = (S, x0.shape[1], h, x0.shape[3]) if layout == "sbhd" else (x0.shape[0], S, h, x0.shape[3])
+        outs.append(torch.empty(shape, dtype=x0.dtype, device=x0.device))
+    return seq_head_permute(shards, outs, 0, layout)
+
+
+def head_to_seq(parts, seq_lens, layout="sbhd"):
+    """parts[r]: rank r's head group; returns rank i's sequence shard with all heads."""
+    H = sum(x.shape[2] for x in parts)
+    outs = []
+    for s in seq_lens:
+        x0 = parts[0]
+        shape = (s, x0.shape[1], H, x0.shape[3]) if layout == "sbhd" else (x0.shape[0], s, H, x0.shape[3])
+        outs.append(torch.empty(shape, dtype=x0.dtype, device=x0.device))
+    return seq_head_permute(parts, outs, 1, layout)

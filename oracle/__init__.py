@@ -21,13 +21,14 @@ Every public function is pinned by ``tests/test_oracle_pins.py`` (closed forms,
 finite differences, a library routine, invariants, page fixtures); none is
 "parity unpinned".
 """
-from .attention import attention_forward, attention_backward, merge_lse
+from .attention import attention_backward, attention_delta, attention_forward, merge_lse
 from .permute import split_sizes, seq_to_head, head_to_seq
 
 __all__ = [
     "attention_forward",
     "attention_backward",
     "merge_lse",
+    "attention_delta",
     "split_sizes",
     "seq_to_head",
     "head_to_seq",

@@ -130,6 +130,19 @@ def attention_backward(q, k, v, dout, scale=None, row_block=4096):
     return dq, dk, dv
 
 
+def attention_delta(out, dout):
+    """Per-row dot product of the output gradient with the output, [B, H, S].
+
+    delta_i = sum_d dout_id * out_id.  For out = attention_forward(q, k, v) this
+    equals rowsum(P * dP) of ``attention_backward`` (since out_i = sum_j P_ij v_j
+    and dP_ij = <dout_i, v_j>), which is how the backward consumes it.
+    """
+    out, dout = _as64(out), _as64(dout)
+    if out.shape != dout.shape or out.ndim != 4:
+        raise ValueError("out and dout must both be [B, S, H, D]")
+    return np.transpose((out * dout).sum(axis=3), (0, 2, 1)).copy()
+
+
 def merge_lse(out_a, lse_a, out_b, lse_b):
     """Merge two partial attention results over disjoint key sets.
 

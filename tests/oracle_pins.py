@@ -259,6 +259,22 @@ def pin_rejects_bad_gqa(o):
     raise AssertionError("H_q % H_kv != 0 must be refused")
 
 
+def pin_delta_identity(o):
+    """delta = rowsum(dout * out) equals rowsum(P * dP) with P from torch.softmax (library)."""
+    r = _rng(14)
+    B, Sq, Sk, Hq, Hkv, D = 2, 7, 9, 4, 2, 6
+    q = r.standard_normal((B, Sq, Hq, D)); k = r.standard_normal((B, Sk, Hkv, D))
+    v = r.standard_normal((B, Sk, Hkv, D)); d = r.standard_normal((B, Sq, Hq, D))
+    out, _ = o.attention_forward(q, k, v, scale=0.3)
+    delta = o.attention_delta(out, d)
+    assert delta.shape == (B, Hq, Sq)
+    qt = torch.tensor(q).transpose(1, 2); kt = torch.tensor(k).transpose(1, 2).repeat_interleave(2, dim=1)
+    vt = torch.tensor(v).transpose(1, 2).repeat_interleave(2, dim=1); dt = torch.tensor(d).transpose(1, 2)
+    P = torch.softmax(0.3 * qt @ kt.transpose(-1, -2), dim=-1)
+    want = (P * (dt @ vt.transpose(-1, -2))).sum(-1).numpy()
+    assert np.abs(delta - want).max() < 1e-12
+
+
 # ----------------------------------------------------------------------------- exchange
 def pin_split_sizes(o):
     assert o.split_sizes(1000, 3) == [334, 333, 333]   # the uneven workload's stated split
@@ -376,7 +392,7 @@ def pin_ulysses_composition(o):
 ALL_PINS = [
     pin_single_key, pin_zero_query, pin_equal_keys, pin_no_keys, pin_default_scale,
     pin_torch_sdpa, pin_finite_differences, pin_chunk_merge_invariance, pin_merge_closed_forms,
-    pin_gradient_invariants, pin_gqa_group_sums, pin_rejects_bad_gqa,
+    pin_gradient_invariants, pin_gqa_group_sums, pin_rejects_bad_gqa, pin_delta_identity,
     pin_split_sizes, pin_exchange_slot_rule, pin_exchange_gradient_2x, pin_page_exchange_shapes,
     pin_ulysses_composition,
 ]

@@ -1,0 +1,209 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/ra.h
+declares, its host helpers agree with the oracle's, and every malformed call is
+refused with a status before anything is launched (no call here reaches HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle_pins import golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+abi = pytest.importorskip("context_attention_lse_kv_amd._abi")
+
+
+def _lib():
+    if not os.path.exists(abi.LIB_PATH):
+        pytest.fail("libra.so is not built (run python -m context_attention_lse_kv_amd.build)")
+    return abi.lib()
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "ra.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\*?\s+\**(ra_[a-z0-9_]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_what_binding_lists():
+    assert declared_symbols() == sorted(abi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_split_sizes_matches_oracle():
+    lib = _lib()
+    for n in list(range(0, 50)) + [512, 1000, 4608, 32768, 32769]:
+        for parts in range(1, 10):
+            buf = (ctypes.c_int32 * parts)()
+            assert lib.ra_split_sizes(n, parts, buf) == abi.RA_OK
+            assert list(buf) == oracle.split_sizes(n, parts)
+
+
+def test_ring_order_starts_local_and_walks_back():
+    lib = _lib()
+    for R in range(1, 9):
+        for rank in range(R):
+            buf = (ctypes.c_int32 * R)()
+            assert lib.ra_ring_order(R, rank, buf) == abi.RA_OK
+            assert list(buf) == [(rank - i) % R for i in range(R)]
+    buf = (ctypes.c_int32 * 8)()
+    lib.ra_ring_order(8, 0, buf)
+    assert list(buf) == [0, 7, 6, 5, 4, 3, 2, 1]
+
+
+# ------------------------------------------------------------------ validation (no launch)
+FAKE = 1 << 20  # 16-byte aligned fake device address: never dereferenced on the error paths below
+
+
+def T(B, S, H, D, dtype=abi.RA_BF16, data=FAKE, strides=None):
+    sB, sS, sH = strides if strides else (S * H * D, H * D, D)
+    return abi.RaTensor(data, dtype, B, S, H, D, sB, sS, sH)
+
+
+def Lrows(B, H, S, data=FAKE):
+    return abi.RaLse(data, B, H, S, H * S, S)
+
+
+def fwd(q, k, v, out, lse, merge=0, scale=0.125):
+    lib = _lib()
+    st = lib.ra_fwd_chunk(q, k, v, scale, out, lse, merge, None)
+    return st, lib.ra_last_error().decode()
+
+
+def good(Sq=64, Sk=64, Hq=8, Hkv=8, D=64):
+    return (T(1, Sq, Hq, D), T(1, Sk, Hkv, D), T(1, Sk, Hkv, D), T(1, Sq, Hq, D, abi.RA_F32), Lrows(1, Hq, Sq))
+
+
+def test_gqa_divisibility_refused_with_page_message():
+    q, k, v, o, l = good(Hq=6, Hkv=4)
+    st, msg = fwd(q, k, v, o, l)
+    assert st == abi.RA_E_SHAPE
+    assert golden()["gqa_divisibility_error"]["message"] in msg
+
+
+@pytest.mark.parametrize("case, status", [
+    ("null_q", abi.RA_E_ARG), ("null_data", abi.RA_E_ARG), ("bad_dtype", abi.RA_E_DTYPE),
+    ("mixed_dtype", abi.RA_E_DTYPE), ("d96", abi.RA_E_UNSUPPORTED), ("misaligned_ptr", abi.RA_E_ALIGN),
+    ("misaligned_stride", abi.RA_E_ALIGN), ("batch_mismatch", abi.RA_E_SHAPE), ("headdim_mismatch", abi.RA_E_SHAPE),
+    ("out_bf16", abi.RA_E_DTYPE), ("out_shape", abi.RA_E_SHAPE), ("lse_shape", abi.RA_E_SHAPE),
+    ("bad_merge", abi.RA_E_ARG), ("neg_scale", abi.RA_E_ARG), ("nan_scale", abi.RA_E_ARG),
+    ("overlap", abi.RA_E_ARG), ("neg_stride", abi.RA_E_ARG), ("zero_heads", abi.RA_E_SHAPE),
+])
+def test_fwd_chunk_refuses(case, status):
+    q, k, v, o, l = good()
+    merge, scale = 0, 0.125
+    if case == "null_q":
+        st = _lib().ra_fwd_chunk(None, k, v, scale, o, l, 0, None)
+        assert st == status
+        return
+    if case == "null_data": q.data = None
+    if case == "bad_dtype": q.dtype = 7
+    if case == "mixed_dtype": k.dtype = abi.RA_F32
+    if case == "d96": q, k, v, o = T(1, 64, 8, 96), T(1, 64, 8, 96), T(1, 64, 8, 96), T(1, 64, 8, 96, abi.RA_F32)
+    if case == "misaligned_ptr": v.data = FAKE + 8
+    if case == "misaligned_stride": q.sS = 8 * 64 + 4
+    if case == "batch_mismatch": k.B = 2
+    if case == "headdim_mismatch": k = T(1, 64, 8, 128)
+    if case == "out_bf16": o.dtype = abi.RA_BF16
+    if case == "out_shape": o.S = 63
+    if case == "lse_shape": l.S = 65
+    if case == "bad_merge": merge = 2
+    if case == "neg_scale": scale = -1.0
+    if case == "nan_scale": scale = float("nan")
+    if case == "overlap": q.sS = 8  # rows alias each other's heads
+    if case == "neg_stride": q.sH = -64
+    if case == "zero_heads": q.H = 0
+    st, msg = fwd(q, k, v, o, l, merge, scale)
+    assert st == status, (case, msg)
+    assert msg
+
+
+def chunks(lens, order):
+    starts = [sum(lens[:i]) for i in range(len(lens))]
+    keep = ((ctypes.c_int32 * len(lens))(*starts), (ctypes.c_int32 * len(lens))(*lens),
+            (ctypes.c_int32 * len(order))(*order))
+    c = abi.RaChunks(len(lens), *keep)
+    c._keep = keep
+    return c
+
+
+@pytest.mark.parametrize("lens, order, status", [
+    ([32, 32], [0, 0], abi.RA_E_ARG),        # order not a permutation
+    ([32, 32], [1, 2], abi.RA_E_ARG),
+    ([32, 31], [0, 1], abi.RA_E_SHAPE),      # does not cover S_k
+    ([32, 40], [0, 1], abi.RA_E_SHAPE),      # runs past S_k
+    ([-1, 65], [0, 1], abi.RA_E_ARG),
+])
+def test_ring_fwd_refuses_bad_chunk_tables(lens, order, status):
+    lib = _lib()
+    q, k, v, o, l = good()
+    c = chunks(lens, order)
+    st = lib.ra_ring_fwd(q, k, v, ctypes.byref(c), 0.125, o, l, None, 0, None)
+    assert st == status, lib.ra_last_error()
+
+
+def test_ring_fwd_refuses_gapped_tiling():
+    lib = _lib()
+    q, k, v, o, l = good()
+    starts, lens, order = (ctypes.c_int32 * 2)(0, 40), (ctypes.c_int32 * 2)(32, 24), (ctypes.c_int32 * 2)(0, 1)
+    c = abi.RaChunks(2, starts, lens, order)
+    assert lib.ra_ring_fwd(q, k, v, ctypes.byref(c), 0.125, o, l, None, 0, None) == abi.RA_E_SHAPE
+
+
+def test_ring_fwd_needs_workspace_for_bf16_out():
+    lib = _lib()
+    q, k, v, _, l = good()
+    o = T(1, 64, 8, 64, abi.RA_BF16)
+    need = lib.ra_ring_fwd_workspace_bytes(q, o)
+    assert need >= 64 * 8 * 64 * 4
+    c = chunks([32, 32], [0, 1])
+    assert lib.ra_ring_fwd(q, k, v, ctypes.byref(c), 0.125, o, l, None, 0, None) == abi.RA_E_WORKSPACE
+    assert lib.ra_ring_fwd(q, k, v, ctypes.byref(c), 0.125, o, l, FAKE, need - 1, None) == abi.RA_E_WORKSPACE
+    assert lib.ra_ring_fwd_workspace_bytes(q, T(1, 64, 8, 64, abi.RA_F32)) == 0
+
+
+def test_ring_bwd_workspace_sizes():
+    lib = _lib()
+    q, k = T(1, 100, 8, 64), T(1, 300, 2, 64)
+    f = lambda t: T(t.B, t.S, t.H, t.D, abi.RA_F32)
+    base = lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k))
+    assert base >= 8 * 100 * 4
+    full = lib.ra_ring_bwd_workspace_bytes(q, k, q, k, k)
+    assert full >= base + (100 * 8 * 64 + 2 * 300 * 2 * 64) * 4
+
+
+def test_bwd_chunk_refuses_bf16_accumulators():
+    lib = _lib()
+    q, k, v = T(1, 64, 8, 64), T(1, 64, 2, 64), T(1, 64, 2, 64)
+    l = Lrows(1, 8, 64)
+    st = lib.ra_bwd_chunk(q, k, v, q, l, l, 0.125, T(1, 64, 8, 64), T(1, 64, 2, 64, abi.RA_F32),
+                          T(1, 64, 2, 64, abi.RA_F32), 0, None)
+    assert st == abi.RA_E_DTYPE
+
+
+def test_permute_refusals():
+    lib = _lib()
+    A = abi.RaTensor * 2
+    ins = A(T(2, 5, 8, 64, data=FAKE), T(2, 5, 8, 64, data=FAKE + (1 << 16)))
+    outs = A(T(2, 10, 4, 64, data=FAKE + (2 << 16)), T(2, 10, 4, 64, data=FAKE + (3 << 16)))
+    bad = A(T(2, 10, 4, 64, data=FAKE + (2 << 16)), T(2, 10, 3, 64, data=FAKE + (3 << 16)))
+    assert lib.ra_seq_head_permute(ins, 2, bad, 2, 0, None) == abi.RA_E_SHAPE   # heads sum to 7
+    assert lib.ra_seq_head_permute(ins, 2, outs, 2, 2, None) == abi.RA_E_ARG    # bad direction
+    assert lib.ra_seq_head_permute(ins, 2, outs, 1, 0, None) == abi.RA_E_ARG    # rank count mismatch
+    alias = A(T(2, 10, 4, 64, data=FAKE), T(2, 10, 4, 64, data=FAKE + (3 << 16)))
+    assert lib.ra_seq_head_permute(ins, 2, alias, 2, 0, None) == abi.RA_E_ARG   # out aliases in
+    short = A(T(2, 9, 4, 64, data=FAKE + (2 << 16)), T(2, 9, 4, 64, data=FAKE + (3 << 16)))
+    assert lib.ra_seq_head_permute(ins, 2, short, 2, 0, None) == abi.RA_E_SHAPE  # 5 + 5 != 9
+
+
+def test_status_strings():
+    lib = _lib()
+    for i, name in enumerate(abi.STATUS_NAMES):
+        assert lib.ra_status_string(i).decode() == name

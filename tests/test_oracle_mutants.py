@@ -29,6 +29,7 @@ MUTANTS = [
     ("attention.py", "wa * out_a + wb * out_b", "wa * out_a + wa * out_b"),
     ("attention.py", "np.logaddexp(lse_a, lse_b)", "np.maximum(lse_a, lse_b)"),
     ("attention.py", "wa = np.transpose(wa, (0, 2, 1))[..., None]", "wa = np.transpose(wb, (0, 2, 1))[..., None]"),
+    ("attention.py", "(out * dout).sum(axis=3), (0, 2, 1)", "(out * dout).sum(axis=3), (0, 1, 2)"),
     ("permute.py", "(1 if i < extra else 0)", "(1 if i >= parts - extra else 0)"),
     ("permute.py", "x[:, :, hoff[r]:hoff[r + 1], :]", "x[:, :, hoff[R - 1 - r]:hoff[R - r], :]"),
     ("permute.py", "y[soff[i]:soff[i + 1]]", "y[soff[i]:soff[i] + seq_lens[0]]"),

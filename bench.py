@@ -1,0 +1,234 @@
+"""Benchmark of the ring-attention hot path on one MI355X.
+
+One step = one ring forward sweep + one ring backward sweep of one rank's
+share: the video-DiT GQA workload (B1, S 32768, H_q 32, H_kv 8, D 128, bf16)
+with the local query shard of 4096 rows swept over the 8 key/value chunks of
+4096 in ring order 0,7,6,...,1.  Inputs are resident in HBM before the timed
+region; the timed region covers every launch of both sweeps (delta, chunk
+steps, merges, finalisation casts).
+
+Prints ONE JSON line.  ``value`` is fwd+bwd TFLOP/s with the attention flop
+count 4*B*Hq*Sq*Sk*D (forward) + 10*B*Hq*Sq*Sk*D (backward, five products
+including the recompute).  ``roofline`` describes the dominant kernel (the
+backward chunk step), timed per launch with HIP events on the stream it runs
+on; ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import context_attention_lse_kv_amd as ra  # noqa: E402
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense MFMA)
+HBM_PEAK_GBS = 8000.0
+METRIC = "ring attn fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+
+
+def flops(B, Hq, Sq, Sk, D):
+    return 4.0 * B * Hq * Sq * Sk * D, 10.0 * B * Hq * Sq * Sk * D
+
+
+def timed(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def event_avg(fn, launches, warmup=2):
+    """Average duration of `fn` (one kernel launch) by HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    s = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(s)
+    for _ in range(launches):
+        fn()
+    end.record(s)
+    end.synchronize()
+    return start.elapsed_time(end) / launches / 1e3  # seconds
+
+
+def setup(Sq_rows, full):
+    w = W.VIDEO_DIT_GQA
+    lens = ra.split_sizes(w.S, w.n_chunks)
+    q, k, v, do = W.make_inputs(w, Sq=w.S if full else Sq_rows)
+    d = torch.device("cuda", 0)
+    gq, gk, gv, gdo = (t.to(d) for t in (q, k, v, do))
+    order = list(range(w.n_chunks)) if full else ra.ring_order(w.n_chunks, 0)
+    return w, lens, order, gq, gk, gv, gdo
+
+
+def run_workload(full, steps, warmup):
+    w, lens, order, q, k, v, do = setup(4096, full)
+    ch = ra.Chunks(lens, order)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((w.B, w.Hq, q.shape[1]), dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty(t.shape, dtype=torch.bfloat16, device=q.device) for t in (q, k, v))
+    # workspaces allocated once, outside the timed region
+    fws = torch.empty(q.numel() * 4 + 256, dtype=torch.uint8, device=q.device)
+    bws = torch.empty(w.B * w.Hq * q.shape[1] * 4 + (q.numel() + 2 * k.numel()) * 4 + 4096, dtype=torch.uint8,
+                      device=q.device)
+
+    def fwd():
+        ra.ring_fwd(q, k, v, ch, out=out, lse=lse, workspace=fws)
+
+    def bwd():
+        ra.ring_bwd(q, k, v, out, do, lse, ch, workspace=bws, dq=dq, dk=dk, dv=dv)
+
+    def step():
+        fwd()
+        bwd()
+
+    t_step = timed(step, steps, warmup)
+    t_fwd = timed(fwd, max(3, steps // 2), 1)
+    t_bwd = timed(bwd, max(3, steps // 2), 1)
+    f_f, f_b = flops(w.B, w.Hq, q.shape[1], w.S, w.D)
+    return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, t_step=t_step, t_fwd=t_fwd,
+                t_bwd=t_bwd, f_f=f_f, f_b=f_b)
+
+
+def dominant_kernel(r, launches=8):
+    """Backward chunk step: one kernel launch per call (accumulate=1 skips the zero fill)."""
+    q, k, v, do, out, lse = r["q"], r["k"], r["v"], r["do"], r["out"], r["lse"]
+    c = r["lens"][0]
+    kc, vc = k[:, :c], v[:, :c]
+    delta = torch.empty_like(lse)
+    ra.bwd_delta(out, do, delta)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.zeros(kc.shape, dtype=torch.float32, device=q.device)
+    dv = torch.zeros_like(dk)
+    t = event_avg(lambda: ra.bwd_chunk(q, kc, vc, do, lse, delta, dq, dk, dv, accumulate=1), launches)
+    w = r["w"]
+    f = 10.0 * w.B * w.Hq * q.shape[1] * c * w.D
+    return t, f
+
+
+def cpu_baseline(target_s=15.0):
+    """The CPU fp64 oracle on a bounded sample: one query head's rows of the shard
+    against the whole 32768-key sequence (its kv head), forward + backward."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = W.VIDEO_DIT_GQA
+    q, k, v, do = W.make_inputs(w, Sq=4096)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    kn, vn = f64(k[:, :, 0:1]), f64(v[:, :, 0:1])
+    rows = 128
+    while True:
+        qn, don = f64(q[:, :rows, 0:1]), f64(do[:, :rows, 0:1])
+        t0 = time.perf_counter()
+        oracle.attention_forward(qn, kn, vn, row_block=128)
+        oracle.attention_backward(qn, kn, vn, don, row_block=128)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or rows >= 4096:
+            break
+        rows = min(4096, rows * 2)
+    fl = 14.0 * 1 * 1 * rows * w.S * w.D
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle fwd+bwd (numpy fp64) of query head 0, rows [0,{rows}) of the rank-0 shard, "
+                      f"against all {w.S} keys of kv head 0; {dt:.2f} s wall; same 14*Sq*Sk*D flop count"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full", action="store_true", help="skip the full-Q sweep (extra field)")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only launch the dominant kernel (for hardware-counter runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB, 3 times (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
+              "(single-GPU build: no collectives)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (HIP device)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib, "launches": 3}))
+        return
+    if args.kernel_only:
+        r = run_workload(False, 1, 0)
+        t_k, f_k = dominant_kernel(r, launches=args.steps)
+        print(json.dumps({"kernel_only": True, "avg_launch_ms": round(t_k * 1e3, 4),
+                          "tflops": round(f_k / t_k / 1e12, 2)}))
+        return
+    r = run_workload(False, args.steps, args.warmup)
+    total = r["f_f"] + r["f_b"]
+    value = total / r["t_step"] / 1e12
+    t_k, f_k = dominant_kernel(r)
+    achieved = f_k / t_k / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["t_step"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "video_dit_gqa_rank0_shard", "B": 1, "S": r["w"].S, "Sq": int(r["q"].shape[1]),
+                   "Hq": r["w"].Hq, "Hkv": r["w"].Hkv, "D": r["w"].D, "chunks": r["lens"], "order": r["order"],
+                   "inputs": "N(0,1) seed 777, bf16"},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(r["f_f"] / r["t_fwd"] / 1e12, 2),
+        "bwd_tflops": round(r["f_b"] / r["t_bwd"] / 1e12, 2),
+        "fwd_ms": round(r["t_fwd"] * 1e3, 4),
+        "bwd_ms": round(r["t_bwd"] * 1e3, 4),
+        "roofline": {"bound": "mfma", "kernel": "bwd_bf16_kernel<128> (one ring step, 4096 q rows x 4096 keys)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(t_k * 1e3, 4),
+                     "traffic": None},
+    }
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_full:
+        rf = run_workload(True, max(3, args.steps // 4), 1)
+        tf = rf["f_f"] + rf["f_b"]
+        res["full_q"] = {"Sq": int(rf["q"].shape[1]), "ms_per_step": round(rf["t_step"] * 1e3, 3),
+                         "tflops": round(tf / rf["t_step"] / 1e12, 2),
+                         "pct_of_peak": round(100.0 * tf / rf["t_step"] / 1e12 / PEAK_BF16_TFLOPS, 2),
+                         "fwd_tflops": round(rf["f_f"] / rf["t_fwd"] / 1e12, 2),
+                         "bwd_tflops": round(rf["f_b"] / rf["t_bwd"] / 1e12, 2)}
+        del rf
+        torch.cuda.empty_cache()
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

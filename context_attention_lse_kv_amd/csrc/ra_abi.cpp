@@ -116,6 +116,16 @@ ra_status check_rows(const ra_lse* l, const char* name, int32_t B, int32_t H, in
     return RA_OK;
 }
 
+// The bf16 kernels address one (batch, head) slice with 32-bit buffer offsets: the
+// slice's byte span, plus one tile of slack, must stay below 2^31.
+ra_status check_span32(const ra_tensor& t, const char* name) {
+    const int64_t span = ((int64_t)(t.S + 128) * t.sS + t.D) * (int64_t)esize(t.dtype);
+    if (span >= ((int64_t)1 << 31))
+        return fail(RA_E_UNSUPPORTED, "%s: one (batch, head) slice spans %lld bytes; the bf16 kernels need < 2^31",
+                    name, (long long)span);
+    return RA_OK;
+}
+
 bool same_shape(const ra_tensor& a, const ra_tensor& b) { return a.B == b.B && a.S == b.S && a.H == b.H && a.D == b.D; }
 
 ra_status check_scale(float scale) {
@@ -137,6 +147,11 @@ ra_status check_qkv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v) 
     if (q->H % k->H != 0)
         return fail(RA_E_SHAPE,
                     "Number of heads in key/value must divide number of heads in query (H_q=%d, H_kv=%d)", q->H, k->H);
+    if (q->dtype == RA_BF16) {
+        RA_TRY(check_span32(*q, "q"));
+        RA_TRY(check_span32(*k, "k"));
+        RA_TRY(check_span32(*v, "v"));
+    }
     return RA_OK;
 }
 

@@ -146,15 +146,17 @@ def ring_fwd(q, k, v, chunks, scale=None, out=None, lse=None, out_dtype=None, la
     return out, lse
 
 
-def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layout="bshd", workspace=None):
-    """Backward sweep in the forward's chunk order; returns (dq, dk, dv)."""
+def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layout="bshd", workspace=None,
+             dq=None, dk=None, dv=None):
+    """Backward sweep in the forward's chunk order; returns (dq, dk, dv) (written into
+    dq/dk/dv when given)."""
     _dev_check(q, k, v, out, dout, lse)
     if not isinstance(chunks, Chunks):
         chunks = Chunks(chunks)
     gd = grad_dtype or q.dtype
-    dq = torch.empty(q.shape, dtype=gd, device=q.device)
-    dk = torch.empty(k.shape, dtype=gd, device=q.device)
-    dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    dq = torch.empty(q.shape, dtype=gd, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=gd, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=gd, device=q.device) if dv is None else dv
     t = [tensor_desc(x, layout) for x in (q, k, v, out, dout, dq, dk, dv)]
     need = lib().ra_ring_bwd_workspace_bytes(t[0], t[1], t[5], t[6], t[7])
     ws = _workspace(workspace, need, q.device)

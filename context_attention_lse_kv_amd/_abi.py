@@ -7,7 +7,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libra.so")
+# RA_LIB selects another build of the same library (e.g. to compare kernel variants)
+LIB_PATH = os.environ.get("RA_LIB") or os.path.join(_PKG, "libra.so")
 
 RA_OK, RA_E_ARG, RA_E_SHAPE, RA_E_DTYPE, RA_E_ALIGN, RA_E_UNSUPPORTED, RA_E_WORKSPACE, RA_E_HIP = range(8)
 RA_BF16, RA_F32 = 1, 2

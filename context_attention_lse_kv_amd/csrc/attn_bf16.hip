@@ -16,15 +16,17 @@
 // diffusers issue "Ring attention backward uses stale iteration-0 KV", table "How
 // it surfaces per backend": ring needs LSE for partial-result merging).
 //
-// Backward (one launch per ring step, against that step's own K/V chunk - the
-// point of that issue's "Root cause" and "Expected behavior"): a workgroup owns
-// 128 keys of the chunk (32 per wavefront, K and V held in registers) for one
-// query head and sweeps all query rows in LDS tiles of 64.  Per tile it
-// recomputes S = Q K^T and dP = dO V^T with the final LSE and delta, forms P and
-// dS, accumulates dV += P^T dO and dK += dS^T Q in registers, and adds
-// dQ += dS K into the fp32 dQ accumulator with atomics after passing dS^T through
-// LDS.  dK/dV are added atomically at the end because the query heads of a GQA
-// group run in different workgroups.
+// Backward (one chunk step against that step's own K/V chunk - the point of that
+// issue's "Root cause" and "Expected behavior") runs as two kernels with no dQ
+// atomics.  The KV-stationary kernel owns 128 keys of the chunk (32 per wavefront, K
+// and V in registers) for one query head, sweeps all query rows in LDS tiles of 64,
+// recomputes S = Q K^T and dP = dO V^T with the final LSE and delta, and accumulates
+// dV += P^T dO and dK += dS^T Q in registers (added atomically at the end, because the
+// query heads of a GQA group run in different workgroups).  The Q-stationary kernel
+// owns 128 query rows like the forward, recomputes S^T and dP^T per key tile and
+// accumulates dQ^T += K^T dS^T in registers, so each row's dQ has a single writer.
+// The recompute of S and dP in both kernels (7 products instead of 5) is cheaper on
+// this chip than adding dQ through device-scope atomics from every key tile.
 //
 // Both kernels stream their tiles with buffer loads (rows past the end of a
 // slice read as zeros, so tails need no branches), keep the next tile in
@@ -67,7 +69,7 @@ struct BwdParams {
     int64_t q_sB, q_sS, q_sH, k_sB, k_sS, k_sH, v_sB, v_sS, v_sH, do_sB, do_sS, do_sH;
     int64_t l_sB, l_sH, d_sB, d_sH;
     int64_t dq_sB, dq_sS, dq_sH, dk_sB, dk_sS, dk_sH, dv_sB, dv_sS, dv_sH;
-    int B, Sq, Sk, Hq, G, n_ktiles;
+    int B, Sq, Sk, Hq, G, n_tiles;  // tiles along the kernel's stationary axis (keys or query rows)
     uint32_t q_bytes, do_bytes, k_bytes, v_bytes;
     float scale, c;
 };
@@ -311,124 +313,172 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 }
 
 // ============================================================================ backward
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
-    constexpr int KS = D / 16, DB = D / 32, BN = kBwdBlockN, BM = kBwdBlockM;
-    constexpr int RB = BM / 32;       // 32-row blocks per Q tile
-    constexpr int QP = D + 8;         // Q / dO tile pitch (row reads and transposing reads)
-    constexpr int KTP = D + 16;       // K tile pitch (transposing reads)
-    constexpr int SP = BM + 16;       // dS^T tile pitch ([key][row], transposing reads)
-    constexpr int QT = BM * QP;
-    constexpr int CHQ = BM * (D / 8) / 256;
-    constexpr int CHK = BN * (D / 8) / 256;
-    constexpr int DQ_TILES = RB * DB / 4;  // dQ 32x32 tiles per wavefront
-    __shared__ __attribute__((aligned(16))) uint16_t smem[BN * KTP + 4 * QT + BN * SP];
-    __shared__ __attribute__((aligned(16))) float stat[2][2][BM];  // [buffer][lse*log2e | delta][row]
-    lds_u16* const Ks = (lds_u16*)smem;
-    lds_u16* const Qs = Ks + BN * KTP;   // [2][BM][QP]
-    lds_u16* const Os = Qs + 2 * QT;     // [2][BM][QP]
-    lds_u16* const dSt = Os + 2 * QT;    // [BN][SP]
+// Row swizzle of the unpadded Q / dO / K tiles in LDS: 16-byte chunk c of tile row r
+// lives at chunk slot c ^ swz(r).  Eight consecutive rows (the 16-byte row reads of an
+// MFMA operand) and the 4 rows x 2 chunks of a transposing read then fall on distinct
+// bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0, `bytes` bytes from base) as four SGPR words.
+__device__ __forceinline__ i32x4_t make_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t d;
+    d[0] = (int)(uint32_t)a;
+    d[1] = (int)((uint32_t)(a >> 32) & 0xffffu);
+    d[2] = (int)bytes;
+    d[3] = 0x00020000;
+    return d;
+}
+
+__device__ __forceinline__ i32x4_t tile_desc(const void* base, int64_t r0, int64_t row_stride_bytes, uint32_t bytes) {
+    const int64_t off = r0 * row_stride_bytes;
+    return make_desc((const char*)base + off, off < (int64_t)bytes ? (uint32_t)(bytes - off) : 0u);
+}
+
+// Asynchronous copy global -> LDS of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l's bytes land at dst + 16 * l, dst being the same for the whole wavefront;
+// bytes past the descriptor's size arrive as zeros.  Issued as inline assembly so
+// that the compiler adds no wait after it: completion is awaited explicitly with
+// wait_vmem() before the barrier that publishes the tile.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4_t desc, RA_LDS void* dst, uint32_t voff) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(desc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(0): this wavefront's buffer loads (incl. the LDS copies) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Copy offsets for a swizzled, unpadded tile: wavefront-wide copy `ci` moves tile rows
+// [ci*RPI, +RPI) (RPI = 1024 / row bytes); lane l takes row ci*RPI + l/RC and the
+// 16-byte chunk (l % RC) ^ swz(row), so that it lands at its swizzled slot.
+template <int D>
+__device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
+    constexpr int RC = D / 8, RPI = 1024 / (D * 2);
+    const int r = ci * RPI + lane / RC;
+    const int c = (lane % RC) ^ swz(r);
+    return (uint32_t)((r * sS + 8 * c) * 2);
+}
+
+// --------------------------------------------------------------- dK, dV (KV-stationary)
+// Workgroup = 128 keys of the chunk (32 per wavefront) x one query head; sweeps every
+// query row of that head in tiles of 64.  No dQ here (see bwd_dq_bf16_kernel), so the
+// only atomics are the final dK/dV adds shared by the query heads of a GQA group.
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
+    constexpr int KS = D / 16, DB = D / 32, BN = kBwdBlockN, BM = kBwdBlockM;
+    constexpr int RB = BM / 32;            // 32-row blocks per Q tile
+    constexpr int RC = D / 8;              // 16-byte chunks per row
+    constexpr int ROWB = D * 2;            // bytes per (unpadded) tile row
+    constexpr int TILEB = BM * ROWB;       // bytes of one Q or dO tile
+    constexpr int RPI = 1024 / ROWB;       // rows moved by one wavefront-wide copy
+    constexpr int NI = BM / RPI / 4;       // copies per wavefront per tensor per tile
+    static_assert(RC >= 8 && NI >= 1, "tile geometry");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [Q0 | dO0 | Q1 | dO1]
+    __shared__ __attribute__((aligned(16))) float stat[2][2][BM];     // [buffer][lse*log2e | delta][row]
+    RA_LDS char* const lbase = (RA_LDS char*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    const int gq = lane >> 4, l16 = lane & 15;
+    const int gq = lane >> 4, l16 = lane & 15, e4 = l16 >> 2, a4 = l16 & 3;
     const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int kt = (int)(logical % p.n_ktiles);
-    const int rest = (int)(logical / p.n_ktiles);
+    const int kt = (int)(logical % p.n_tiles);
+    const int rest = (int)(logical / p.n_tiles);
     const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
     const int n0 = kt * BN;
     const int key = n0 + 32 * w + l32;  // this lane's key (column of S/dP, row of dK/dV)
     const bool key_ok = key < p.Sk;
     const bool keys_partial = n0 + BN > p.Sk;
 
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH, p.k_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH, p.v_bytes);
+    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
+    const uint16_t* vbase = p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
     const uint16_t* qbase = p.q + (int64_t)b * p.q_sB + (int64_t)h * p.q_sH;
     const uint16_t* obase = p.dout + (int64_t)b * p.do_sB + (int64_t)h * p.do_sH;
-    const float* lbase = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH;
-    const float* dbase = p.delta + (int64_t)b * p.d_sB + (int64_t)h * p.d_sH;
+    const float* lbase_g = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH;
+    const float* dbase_g = p.delta + (int64_t)b * p.d_sB + (int64_t)h * p.d_sH;
 
-    // K rows of the workgroup (for dQ), and this lane's K and V rows as MFMA operands
-#pragma unroll
-    for (int j = 0; j < CHK; ++j) {
-        const int c = tid + 256 * j, r = c / (D / 8), c8 = c % (D / 8);
-        *(RA_LDS u32x4_t*)(Ks + r * KTP + 8 * c8) = bload16(rk, (uint32_t)(((n0 + r) * p.k_sS + 8 * c8) * 2), 0);
-    }
     bf16x8_t kreg[KS], vreg[KS];
+    {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, 0, p.k_sS * 2, p.k_bytes);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, 0, p.v_sS * 2, p.v_bytes);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        kreg[ks] = as_bf16x8(bload16(rk, (uint32_t)((key * p.k_sS + 16 * ks + 8 * hh) * 2), 0));
-        vreg[ks] = as_bf16x8(bload16(rv, (uint32_t)((key * p.v_sS + 16 * ks + 8 * hh) * 2), 0));
+        for (int ks = 0; ks < KS; ++ks) {
+            kreg[ks] = as_bf16x8(bload16(rk, (uint32_t)((key * p.k_sS + 16 * ks + 8 * hh) * 2), 0));
+            vreg[ks] = as_bf16x8(bload16(rv, (uint32_t)((key * p.v_sS + 16 * ks + 8 * hh) * 2), 0));
+        }
     }
+    uint32_t vq[NI], vo[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        vq[i] = copy_voff<D>(w * NI + i, lane, p.q_sS);
+        vo[i] = copy_voff<D>(w * NI + i, lane, p.do_sS);
+    }
+    float lpre = 0.f, dpre = 0.f;
+    auto issue = [&](int it, int buf) {
+        const int r0 = it * BM;
+        const i32x4_t rq = tile_desc(qbase, r0, p.q_sS * 2, p.q_bytes);
+        const i32x4_t ro = tile_desc(obase, r0, p.do_sS * 2, p.do_bytes);
+        RA_LDS char* qdst = lbase + (2 * buf) * TILEB;
+        RA_LDS char* odst = lbase + (2 * buf + 1) * TILEB;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            dma16(rq, qdst + (w * NI + i) * 1024, vq[i]);
+            dma16(ro, odst + (w * NI + i) * 1024, vo[i]);
+        }
+        if (tid < BM) {
+            const uint32_t nbytes = (uint32_t)p.Sq * 4;
+            lpre = bload4f(tile_rsrc(lbase_g, r0, 4, nbytes), (uint32_t)tid * 4, 0);
+            dpre = bload4f(tile_rsrc(dbase_g, r0, 4, nbytes), (uint32_t)tid * 4, 0);
+        }
+    };
+    auto commit_stats = [&](int buf) {
+        if (tid < BM) {
+            stat[buf][0][tid] = lpre * kLog2e;
+            stat[buf][1][tid] = dpre;
+        }
+    };
+
     f32x16_t dkacc[DB], dvacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         dkacc[db] = f32x16_t{};
         dvacc[db] = f32x16_t{};
     }
+    // lane-constant LDS offsets: row reads (S, dP operands) and transposing reads (dV, dK)
+    const int sw_row = swz(l32);
+    int ra_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
+    const int sw_tr = swz(4 * hh + e4);
+    int tr_off[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
 
-    uint32_t vq[CHQ], vo[CHQ];
-    int lo[CHQ];
-#pragma unroll
-    for (int j = 0; j < CHQ; ++j) {
-        const int c = tid + 256 * j, r = c / (D / 8), c8 = c % (D / 8);
-        vq[j] = (uint32_t)((r * p.q_sS + 8 * c8) * 2);
-        vo[j] = (uint32_t)((r * p.do_sS + 8 * c8) * 2);
-        lo[j] = r * QP + 8 * c8;
-    }
-    u32x4_t qpre[CHQ], opre[CHQ];
-    float lpre = 0.f, dpre = 0.f;
-    auto issue = [&](int it) {
-        const int r0 = it * BM;
-        const __amdgpu_buffer_rsrc_t rq = tile_rsrc(qbase, r0, p.q_sS * 2, p.q_bytes);
-        const __amdgpu_buffer_rsrc_t ro = tile_rsrc(obase, r0, p.do_sS * 2, p.do_bytes);
-#pragma unroll
-        for (int j = 0; j < CHQ; ++j) {
-            qpre[j] = bload16(rq, vq[j], 0);
-            opre[j] = bload16(ro, vo[j], 0);
-        }
-        if (tid < BM) {
-            const uint32_t nbytes = (uint32_t)p.Sq * 4;
-            lpre = bload4f(tile_rsrc(lbase, r0, 4, nbytes), (uint32_t)tid * 4, 0);
-            dpre = bload4f(tile_rsrc(dbase, r0, 4, nbytes), (uint32_t)tid * 4, 0);
-        }
-    };
-    auto commit = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < CHQ; ++j) {
-            *(RA_LDS u32x4_t*)(Qs + buf * QT + lo[j]) = qpre[j];
-            *(RA_LDS u32x4_t*)(Os + buf * QT + lo[j]) = opre[j];
-        }
-        if (tid < BM) {
-            stat[buf][0][tid] = lpre * kLog2e;
-            stat[buf][1][tid] = dpre;
-        }
-    };
-    // lane-constant parts of transposing-read addresses
-    const int trQ = (4 * hh + (l16 >> 2)) * QP + 16 * (gq & 1) + 4 * (l16 & 3);       // dO^T / Q^T operands
-    const int trS = (8 * hh + (l16 >> 2)) * SP + 16 * (gq & 1) + 4 * (l16 & 3);       // dS operand
-    const int trK = (8 * hh + (l16 >> 2)) * KTP + 16 * (gq & 1) + 4 * (l16 & 3);      // K operand of dQ
-    float* dqbase = p.dq + (int64_t)b * p.dq_sB + (int64_t)h * p.dq_sH;
-
-    issue(0);
-    commit(0);
+    issue(0, 0);
+    wait_vmem();
+    commit_stats(0);
     __syncthreads();
     const int ntiles = (p.Sq + BM - 1) / BM;
     for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1, i0 = it * BM;
+        const int buf = it & 1;
         const bool more = it + 1 < ntiles;
-        if (more) issue(it + 1);
-        const lds_u16* qb = Qs + buf * QT;
-        const lds_u16* ob = Os + buf * QT;
-
-        u32x4_t pp[RB][2], pd[RB][2];
+        if (more) issue(it + 1, buf ^ 1);
+        const RA_LDS char* qb = lbase + (2 * buf) * TILEB;
+        const RA_LDS char* ob = lbase + (2 * buf + 1) * TILEB;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             f32x16_t sacc = f32x16_t{}, dpacc = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sacc = mfma32(lds_b128(qb + (32 * rb + l32) * QP + 16 * ks + 8 * hh), kreg[ks], sacc);
-                dpacc = mfma32(lds_b128(ob + (32 * rb + l32) * QP + 16 * ks + 8 * hh), vreg[ks], dpacc);
+                sacc = mfma32(lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks])), kreg[ks], sacc);
+                dpacc = mfma32(lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks])), vreg[ks], dpacc);
             }
             // lane = key, register r = row 32*rb + 8*(r/4) + 4*hh + r%4
             float pv[16], dsv[16];
@@ -437,72 +487,41 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
                 const f32x4_t l2 = *(const RA_LDS f32x4_t*)&stat[buf][0][32 * rb + 8 * g4 + 4 * hh];
                 const f32x4_t dl = *(const RA_LDS f32x4_t*)&stat[buf][1][32 * rb + 8 * g4 + 4 * hh];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g4 + j;
-                    pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], p.c, -l2[j]));
-                }
+                for (int j = 0; j < 4; ++j)
+                    pv[4 * g4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g4 + j], p.c, -l2[j]));
                 if (keys_partial) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) pv[4 * g4 + j] = key_ok ? pv[4 * g4 + j] : 0.f;
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * g4 + j;
-                    dsv[r] = pv[r] * (dpacc[r] - dl[j]);
-                }
+                for (int j = 0; j < 4; ++j) dsv[4 * g4 + j] = pv[4 * g4 + j] * (dpacc[4 * g4 + j] - dl[j]);
             }
-#pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pp[rb][t2][j] = pack_bf16x2(pv[8 * t2 + 2 * j], pv[8 * t2 + 2 * j + 1]);
-                    pd[rb][t2][j] = pack_bf16x2(dsv[8 * t2 + 2 * j], dsv[8 * t2 + 2 * j + 1]);
-                }
-            // dS^T rows for the dQ product: 4 consecutive query rows per 8-byte write
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4)
-                *(RA_LDS u32x2_t*)(dSt + (32 * w + l32) * SP + 32 * rb + 8 * g4 + 4 * hh) =
-                    u32x2_t{pd[rb][g4 / 2][2 * (g4 % 2)], pd[rb][g4 / 2][2 * (g4 % 2) + 1]};
-        }
-        // dV += P^T dO, dK += dS^T Q (k = query rows, 2 k-steps of 16 per row block)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+            // dV += P^T dO, dK += dS^T Q (k = query rows, 2 k-steps of 16)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-                const bf16x8_t pa = as_bf16x8(pp[rb][t2]);
-                const bf16x8_t da = as_bf16x8(pd[rb][t2]);
-                const int off = trQ + (32 * rb + 16 * t2) * QP;
+                u32x4_t pp, pd;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pp[j] = pack_bf16x2(pv[8 * t2 + 2 * j], pv[8 * t2 + 2 * j + 1]);
+                    pd[j] = pack_bf16x2(dsv[8 * t2 + 2 * j], dsv[8 * t2 + 2 * j + 1]);
+                }
+                const bf16x8_t pa = as_bf16x8(pp), da = as_bf16x8(pd);
+                const int roff = (32 * rb + 16 * t2) * ROWB;
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dvacc[db] = mfma32(pa, lds_tr_split8<QP>(ob + off + 32 * db), dvacc[db]);
-                    dkacc[db] = mfma32(da, lds_tr_split8<QP>(qb + off + 32 * db), dkacc[db]);
+                    const u32x2_t o0 = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
+                    const u32x2_t o1 = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off[db]));
+                    dvacc[db] = mfma32(pa, as_bf16x8(u32x4_t{o0[0], o0[1], o1[0], o1[1]}), dvacc[db]);
+                    const u32x2_t q0 = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
+                    const u32x2_t q1 = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off[db]));
+                    dkacc[db] = mfma32(da, as_bf16x8(u32x4_t{q0[0], q0[1], q1[0], q1[1]}), dkacc[db]);
                 }
             }
-        __syncthreads();
-        // dQ[rows][d] += scale * dS K over the workgroup's 128 keys
-        const bool rows_full = i0 + BM <= p.Sq;
-#pragma unroll
-        for (int j = 0; j < DQ_TILES; ++j) {
-            const int ti = w + 4 * j;
-            const int rb = ti % RB, db = ti / RB;
-            f32x16_t acc = f32x16_t{};
-#pragma unroll
-            for (int t = 0; t < BN / 16; ++t)
-                acc = mfma32(lds_tr_cont8<SP>(dSt + trS + 16 * t * SP + 32 * rb),
-                             lds_tr_cont8<KTP>(Ks + trK + 16 * t * KTP + 32 * db), acc);
-            float* dst = dqbase + (int64_t)(i0 + 32 * rb + 4 * hh) * p.dq_sS + 32 * db + l32;
-            if (rows_full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    unsafeAtomicAdd(dst + (int64_t)(8 * (r / 4) + (r % 4)) * p.dq_sS, p.scale * acc[r]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (i0 + 32 * rb + 8 * (r / 4) + 4 * hh + (r % 4) < p.Sq)
-                        unsafeAtomicAdd(dst + (int64_t)(8 * (r / 4) + (r % 4)) * p.dq_sS, p.scale * acc[r]);
-            }
         }
-        if (more) commit(buf ^ 1);
+        if (more) {
+            wait_vmem();
+            commit_stats(buf ^ 1);
+        }
         __syncthreads();
     }
 
@@ -518,6 +537,149 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdParams p) {
                 unsafeAtomicAdd(dkb + (int64_t)kr * p.dk_sS + 32 * db, p.scale * dkacc[db][r]);
                 unsafeAtomicAdd(dvb + (int64_t)kr * p.dv_sS + 32 * db, dvacc[db][r]);
             }
+        }
+}
+
+// --------------------------------------------------------------- dQ (Q-stationary)
+// Workgroup = 128 query rows (32 per wavefront, Q and dO rows in registers) of one
+// query head; sweeps the chunk's keys in tiles of 64 like the forward.  Per tile:
+// S^T = K Q^T and dP^T = V dO^T (lane = query row), P^T and dS^T with the final LSE and
+// delta, then dQ^T += K^T dS^T with K^T read transposed from the K tile.  Each row's
+// dQ is owned by one lane pair, so the fp32 accumulator is updated without atomics.
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
+    constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
+    constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
+    constexpr int RPI = 1024 / ROWB, NI = BN / RPI / 4;
+    static_assert(RC >= 8 && NI >= 1, "tile geometry");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [K0 | V0 | K1 | V1]
+    RA_LDS char* const lbase = (RA_LDS char*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int gq = lane >> 4, l16 = lane & 15, e4 = l16 >> 2, a4 = l16 & 3;
+    const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = (int)(logical % p.n_tiles);
+    const int rest = (int)(logical / p.n_tiles);
+    const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
+    const int row = qt * BM + 32 * w + l32;
+    const bool row_ok = row < p.Sq;
+
+    bf16x8_t qreg[KS], oreg[KS];
+    {
+        const uint16_t* qrow = p.q + (int64_t)b * p.q_sB + (int64_t)row * p.q_sS + (int64_t)h * p.q_sH;
+        const uint16_t* orow = p.dout + (int64_t)b * p.do_sB + (int64_t)row * p.do_sS + (int64_t)h * p.do_sH;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qreg[ks] = as_bf16x8(row_ok ? *(const u32x4_t*)(qrow + 16 * ks + 8 * hh) : z);
+            oreg[ks] = as_bf16x8(row_ok ? *(const u32x4_t*)(orow + 16 * ks + 8 * hh) : z);
+        }
+    }
+    // rows past the end get P = 0 through an infinite LSE
+    const float lse2 = row_ok ? p.lse[(int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row] * kLog2e : INFINITY;
+    const float dl = row_ok ? p.delta[(int64_t)b * p.d_sB + (int64_t)h * p.d_sH + row] : 0.f;
+
+    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
+    const uint16_t* vbase = p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
+    uint32_t vk[NI], vv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        vk[i] = copy_voff<D>(w * NI + i, lane, p.k_sS);
+        vv[i] = copy_voff<D>(w * NI + i, lane, p.v_sS);
+    }
+    auto issue = [&](int it, int buf) {
+        const int r0 = it * BN;
+        const i32x4_t rk = tile_desc(kbase, r0, p.k_sS * 2, p.k_bytes);
+        const i32x4_t rv = tile_desc(vbase, r0, p.v_sS * 2, p.v_bytes);
+        RA_LDS char* kdst = lbase + (2 * buf) * TILEB;
+        RA_LDS char* vdst = lbase + (2 * buf + 1) * TILEB;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
+            dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
+        }
+    };
+    const int sw_row = swz(l32);
+    int ra_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
+    const int sw_tr = swz(4 * hh + e4);
+    int tr_off[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+
+    f32x16_t dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqacc[db] = f32x16_t{};
+
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    const int ntiles = (p.Sk + BN - 1) / BN;
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1, n0 = it * BN;
+        const bool more = it + 1 < ntiles;
+        if (more) issue(it + 1, buf ^ 1);
+        const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
+        const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
+        // S^T = K Q^T and dP^T = V dO^T for two 32-key blocks (lane = query row)
+        f32x16_t sacc[2], dpacc[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            sacc[kb2] = f32x16_t{};
+            dpacc[kb2] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc[kb2] = mfma32(lds_b128((const lds_u16*)(kb + kb2 * 32 * ROWB + ra_off[ks])), qreg[ks], sacc[kb2]);
+                dpacc[kb2] = mfma32(lds_b128((const lds_u16*)(vb + kb2 * 32 * ROWB + ra_off[ks])), oreg[ks], dpacc[kb2]);
+            }
+        }
+        if (n0 + BN > p.Sk) {  // last tile: keys past the chunk read as zero; give them P = 0
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
+        }
+        // dS^T = P^T * (dP^T - delta), packed as the B operand of dQ^T += K^T dS^T
+        u32x4_t dsk[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 8 * (t % 2) + 2 * j;
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -lse2));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -lse2));
+                dsk[t][j] = pack_bf16x2(p0 * (dpacc[t / 2][r] - dl), p1 * (dpacc[t / 2][r + 1] - dl));
+            }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8_t bds = as_bf16x8(dsk[t]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x2_t k0 = lds_tr((const lds_u16*)(kb + 16 * t * ROWB + tr_off[db]));
+                const u32x2_t k1 = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off[db]));
+                dqacc[db] = mfma32(as_bf16x8(u32x4_t{k0[0], k0[1], k1[0], k1[1]}), bds, dqacc[db]);
+            }
+        }
+        if (more) wait_vmem();
+        __syncthreads();
+    }
+    if (!row_ok) return;
+    // dQ^T accumulator: lane = row, register r = d 32*db + 8*(r/4) + 4*hh + r%4
+    float* dqrow = p.dq + (int64_t)b * p.dq_sB + (int64_t)row * p.dq_sS + (int64_t)h * p.dq_sH;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4_t* pq = (f32x4_t*)(dqrow + 32 * db + 8 * g4 + 4 * hh);
+            f32x4_t v4 = *pq;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] += p.scale * dqacc[db][4 * g4 + j];
+            *pq = v4;
         }
 }
 
@@ -577,16 +739,24 @@ hipError_t launch_bwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     p.dk_sB = dk_acc.sB; p.dk_sS = dk_acc.sS; p.dk_sH = dk_acc.sH;
     p.dv_sB = dv_acc.sB; p.dv_sS = dv_acc.sS; p.dv_sH = dv_acc.sH;
     p.B = q.B; p.Sq = q.S; p.Sk = k.S; p.Hq = q.H; p.G = q.H / k.H;
-    p.n_ktiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
     p.q_bytes = span_bytes(q.S, q.sS, q.D);
     p.do_bytes = span_bytes(dout.S, dout.sS, dout.D);
     p.k_bytes = span_bytes(k.S, k.sS, k.D);
     p.v_bytes = span_bytes(v.S, v.sS, v.D);
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
-    const unsigned nb = (unsigned)p.n_ktiles * q.H * q.B;
-    if (q.D == 64) bwd_bf16_kernel<64><<<nb, 256, 0, s>>>(p);
-    else bwd_bf16_kernel<128><<<nb, 256, 0, s>>>(p);
+    // dK/dV: one workgroup per (128-key tile, query head)
+    p.n_tiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
+    const unsigned nkv = (unsigned)p.n_tiles * q.H * q.B;
+    if (q.D == 64) bwd_kv_bf16_kernel<64><<<nkv, 256, 0, s>>>(p);
+    else bwd_kv_bf16_kernel<128><<<nkv, 256, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dQ: one workgroup per (128-row query tile, query head)
+    p.n_tiles = (q.S + kFwdBlockM - 1) / kFwdBlockM;
+    const unsigned ndq = (unsigned)p.n_tiles * q.H * q.B;
+    if (q.D == 64) bwd_dq_bf16_kernel<64><<<ndq, 256, 0, s>>>(p);
+    else bwd_dq_bf16_kernel<128><<<ndq, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 

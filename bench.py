@@ -103,24 +103,51 @@ def run_workload(full, steps, warmup):
 
 
 def dominant_kernel(r, launches=8):
-    """Backward chunk step: one kernel launch per call (accumulate=1 skips the zero fill)."""
+    """The dK/dV half of the backward chunk step (one kernel launch per call with
+    accumulate=1, which skips the zero fill).  It executes S = Q K^T, dP = dO V^T,
+    dV = P^T dO and dK = dS^T Q: 8*D flop per (query row, key) pair per head."""
     q, k, v, do, out, lse = r["q"], r["k"], r["v"], r["do"], r["out"], r["lse"]
     c = r["lens"][0]
     kc, vc = k[:, :c], v[:, :c]
     delta = torch.empty_like(lse)
     ra.bwd_delta(out, do, delta)
-    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.zeros(kc.shape, dtype=torch.float32, device=q.device)
     dv = torch.zeros_like(dk)
-    t = event_avg(lambda: ra.bwd_chunk(q, kc, vc, do, lse, delta, dq, dk, dv, accumulate=1), launches)
+    t = event_avg(lambda: ra.bwd_chunk_dkdv(q, kc, vc, do, lse, delta, dk, dv, accumulate=1), launches)
     w = r["w"]
-    f = 10.0 * w.B * w.Hq * q.shape[1] * c * w.D
+    f = 8.0 * w.B * w.Hq * q.shape[1] * c * w.D
     return t, f
 
 
-def cpu_baseline(target_s=15.0):
-    """The CPU fp64 oracle on a bounded sample: one query head's rows of the shard
-    against the whole 32768-key sequence (its kv head), forward + backward."""
+KERNEL_SRC = os.path.join(ROOT, "context_attention_lse_kv_amd", "csrc", "attn_bf16.hip")
+PROFILE = os.path.join(ROOT, "profiles", "bwd_kv_bf16_video_dit_shard.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter profile,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        vals = {}
+        with open(PROFILE) as f:
+            for line in f:
+                if ":" in line:
+                    k, _, v = line.partition(":")
+                    vals[k.strip()] = v.strip()
+        if vals.get("kernel_source_sha256_16") != sha:
+            return None
+        return int(vals["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(target_s=10.0):
+    """The CPU fp64 oracle, as it stands, on a bounded sample of the workload: whole
+    query heads of the rank-0 shard (4096 rows each, against all 32768 keys of the
+    head's kv head), forward + backward, one head after another until at least
+    `target_s` seconds have been spent."""
     import numpy as np
     import oracle
     try:
@@ -131,21 +158,22 @@ def cpu_baseline(target_s=15.0):
     w = W.VIDEO_DIT_GQA
     q, k, v, do = W.make_inputs(w, Sq=4096)
     f64 = lambda t: t.float().numpy().astype(np.float64)
-    kn, vn = f64(k[:, :, 0:1]), f64(v[:, :, 0:1])
-    rows = 128
-    while True:
-        qn, don = f64(q[:, :rows, 0:1]), f64(do[:, :rows, 0:1])
+    G = w.Hq // w.Hkv
+    heads, spent = 0, 0.0
+    while spent < target_s and heads < w.Hq:
+        h = heads
+        qn, don = f64(q[:, :, h:h + 1]), f64(do[:, :, h:h + 1])
+        kn, vn = f64(k[:, :, h // G:h // G + 1]), f64(v[:, :, h // G:h // G + 1])
         t0 = time.perf_counter()
-        oracle.attention_forward(qn, kn, vn, row_block=128)
-        oracle.attention_backward(qn, kn, vn, don, row_block=128)
-        dt = time.perf_counter() - t0
-        if dt >= target_s / 3 or rows >= 4096:
-            break
-        rows = min(4096, rows * 2)
-    fl = 14.0 * 1 * 1 * rows * w.S * w.D
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle fwd+bwd (numpy fp64) of query head 0, rows [0,{rows}) of the rank-0 shard, "
-                      f"against all {w.S} keys of kv head 0; {dt:.2f} s wall; same 14*Sq*Sk*D flop count"}
+        oracle.attention_forward(qn, kn, vn, row_block=256)
+        oracle.attention_backward(qn, kn, vn, don, row_block=256)
+        spent += time.perf_counter() - t0
+        heads += 1
+    fl = 14.0 * heads * q.shape[1] * w.S * w.D
+    return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle fwd+bwd (numpy fp64) of query heads 0..{heads - 1} of the rank-0 shard "
+                      f"({q.shape[1]} rows each, all {w.S} keys of the head's kv head); {spent:.1f} s wall; "
+                      f"same 14*Sq*Sk*D flop count"}
 
 
 def main():
@@ -209,10 +237,10 @@ def main():
         "bwd_tflops": round(r["f_b"] / r["t_bwd"] / 1e12, 2),
         "fwd_ms": round(r["t_fwd"] * 1e3, 4),
         "bwd_ms": round(r["t_bwd"] * 1e3, 4),
-        "roofline": {"bound": "mfma", "kernel": "bwd_bf16_kernel<128> (one ring step, 4096 q rows x 4096 keys)",
+        "roofline": {"bound": "mfma", "kernel": "bwd_kv_bf16_kernel<128> (dK/dV of one ring step: 4096 q rows x 4096 keys x 32 heads)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(t_k * 1e3, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
     }
     del r
     torch.cuda.empty_cache()

@@ -3,8 +3,8 @@
 The computation lives in ``libra.so`` (HIP kernels for gfx950 behind the C ABI of
 ``include/ra.h``); this package only marshals torch tensors into that ABI.
 """
-from .ops import (Chunks, bwd_chunk, bwd_delta, fwd_chunk, head_to_seq, merge_lse, ring_bwd, ring_fwd,
+from .ops import (Chunks, bwd_chunk, bwd_chunk_dkdv, bwd_chunk_dq, bwd_delta, fwd_chunk, head_to_seq, merge_lse, ring_bwd, ring_fwd,
                   ring_order, rows_desc, seq_head_permute, seq_to_head, split_sizes, tensor_desc)
 
-__all__ = ["Chunks", "bwd_chunk", "bwd_delta", "fwd_chunk", "head_to_seq", "merge_lse", "ring_bwd", "ring_fwd",
+__all__ = ["Chunks", "bwd_chunk", "bwd_chunk_dkdv", "bwd_chunk_dq", "bwd_delta", "fwd_chunk", "head_to_seq", "merge_lse", "ring_bwd", "ring_fwd",
            "ring_order", "rows_desc", "seq_head_permute", "seq_to_head", "split_sizes", "tensor_desc"]

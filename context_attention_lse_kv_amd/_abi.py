@@ -17,7 +17,8 @@ STATUS_NAMES = ["RA_OK", "RA_E_ARG", "RA_E_SHAPE", "RA_E_DTYPE", "RA_E_ALIGN", "
 
 # every symbol include/ra.h declares
 EXPORTS = [
-    "ra_fwd_chunk", "ra_merge_lse", "ra_bwd_delta", "ra_bwd_chunk", "ra_ring_fwd", "ra_ring_bwd",
+    "ra_fwd_chunk", "ra_merge_lse", "ra_bwd_delta", "ra_bwd_chunk", "ra_bwd_chunk_dkdv", "ra_bwd_chunk_dq",
+    "ra_ring_fwd", "ra_ring_bwd",
     "ra_ring_fwd_workspace_bytes", "ra_ring_bwd_workspace_bytes", "ra_seq_head_permute",
     "ra_split_sizes", "ra_ring_order", "ra_status_string", "ra_last_error", "ra_version",
 ]
@@ -50,6 +51,8 @@ _SIGS = {
     "ra_merge_lse": (i32, [T, L, T, L, vp]),
     "ra_bwd_delta": (i32, [T, T, L, vp]),
     "ra_bwd_chunk": (i32, [T, T, T, T, L, L, f32, T, T, T, i32, vp]),
+    "ra_bwd_chunk_dkdv": (i32, [T, T, T, T, L, L, f32, T, T, i32, vp]),
+    "ra_bwd_chunk_dq": (i32, [T, T, T, T, L, L, f32, T, vp]),
     "ra_ring_fwd": (i32, [T, T, T, C, f32, T, L, vp, sz, vp]),
     "ra_ring_bwd": (i32, [T, T, T, T, T, L, C, f32, T, T, T, vp, sz, vp]),
     "ra_ring_fwd_workspace_bytes": (sz, [T, T]),

@@ -715,10 +715,9 @@ hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                                 const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                                 const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s) {
-    if (q.S == 0 || k.S == 0) return hipSuccess;
+namespace {
+BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                     const ra_lse& lse, const ra_lse& delta, float scale) {
     BwdParams p;
     p.q = (const uint16_t*)q.data;
     p.k = (const uint16_t*)k.data;
@@ -726,37 +725,55 @@ hipError_t launch_bwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     p.dout = (const uint16_t*)dout.data;
     p.lse = lse.data;
     p.delta = delta.data;
-    p.dq = (float*)dq_acc.data;
-    p.dk = (float*)dk_acc.data;
-    p.dv = (float*)dv_acc.data;
+    p.dq = p.dk = p.dv = nullptr;
     p.q_sB = q.sB; p.q_sS = q.sS; p.q_sH = q.sH;
     p.k_sB = k.sB; p.k_sS = k.sS; p.k_sH = k.sH;
     p.v_sB = v.sB; p.v_sS = v.sS; p.v_sH = v.sH;
     p.do_sB = dout.sB; p.do_sS = dout.sS; p.do_sH = dout.sH;
     p.l_sB = lse.sB; p.l_sH = lse.sH;
     p.d_sB = delta.sB; p.d_sH = delta.sH;
-    p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
-    p.dk_sB = dk_acc.sB; p.dk_sS = dk_acc.sS; p.dk_sH = dk_acc.sH;
-    p.dv_sB = dv_acc.sB; p.dv_sS = dv_acc.sS; p.dv_sH = dv_acc.sH;
+    p.dq_sB = p.dq_sS = p.dq_sH = p.dk_sB = p.dk_sS = p.dk_sH = p.dv_sB = p.dv_sS = p.dv_sH = 0;
     p.B = q.B; p.Sq = q.S; p.Sk = k.S; p.Hq = q.H; p.G = q.H / k.H;
+    p.n_tiles = 0;
     p.q_bytes = span_bytes(q.S, q.sS, q.D);
     p.do_bytes = span_bytes(dout.S, dout.sS, dout.D);
     p.k_bytes = span_bytes(k.S, k.sS, k.D);
     p.v_bytes = span_bytes(v.S, v.sS, v.D);
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
-    // dK/dV: one workgroup per (128-key tile, query head)
+    return p;
+}
+}  // namespace
+
+hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                                const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
+                                const ra_tensor& dv_acc, hipStream_t s) {
+    if (q.S == 0 || k.S == 0) return hipSuccess;
+    BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
+    p.dk = (float*)dk_acc.data;
+    p.dv = (float*)dv_acc.data;
+    p.dk_sB = dk_acc.sB; p.dk_sS = dk_acc.sS; p.dk_sH = dk_acc.sH;
+    p.dv_sB = dv_acc.sB; p.dv_sS = dv_acc.sS; p.dv_sH = dv_acc.sH;
+    // one workgroup per (128-key tile, query head)
     p.n_tiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
-    const unsigned nkv = (unsigned)p.n_tiles * q.H * q.B;
-    if (q.D == 64) bwd_kv_bf16_kernel<64><<<nkv, 256, 0, s>>>(p);
-    else bwd_kv_bf16_kernel<128><<<nkv, 256, 0, s>>>(p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // dQ: one workgroup per (128-row query tile, query head)
+    const unsigned nb = (unsigned)p.n_tiles * q.H * q.B;
+    if (q.D == 64) bwd_kv_bf16_kernel<64><<<nb, 256, 0, s>>>(p);
+    else bwd_kv_bf16_kernel<128><<<nb, 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                              const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
+                              hipStream_t s) {
+    if (q.S == 0 || k.S == 0) return hipSuccess;
+    BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
+    p.dq = (float*)dq_acc.data;
+    p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
+    // one workgroup per (128-row query tile, query head)
     p.n_tiles = (q.S + kFwdBlockM - 1) / kFwdBlockM;
-    const unsigned ndq = (unsigned)p.n_tiles * q.H * q.B;
-    if (q.D == 64) bwd_dq_bf16_kernel<64><<<ndq, 256, 0, s>>>(p);
-    else bwd_dq_bf16_kernel<128><<<ndq, 256, 0, s>>>(p);
+    const unsigned nb = (unsigned)p.n_tiles * q.H * q.B;
+    if (q.D == 64) bwd_dq_bf16_kernel<64><<<nb, 256, 0, s>>>(p);
+    else bwd_dq_bf16_kernel<128><<<nb, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -215,21 +215,25 @@ hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                                const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s) {
+hipError_t launch_bwd_dq_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                             const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
+                             hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
-    const int T = q.D / kSub;
-    const int rpb = kThreads / T;
-    dim3 gq((q.S + rpb - 1) / rpb, q.H, q.B);
-    dim3 gk((k.S + rpb - 1) / rpb, k.H, k.B);
-    if (q.D == 64) {
-        bwd_dq_f32_kernel<64><<<gq, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
-        bwd_dkdv_f32_kernel<64><<<gk, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
-    } else {
-        bwd_dq_f32_kernel<128><<<gq, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
-        bwd_dkdv_f32_kernel<128><<<gk, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
-    }
+    const int rpb = kThreads / (q.D / kSub);
+    dim3 g((q.S + rpb - 1) / rpb, q.H, q.B);
+    if (q.D == 64) bwd_dq_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
+    else bwd_dq_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                               const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
+                               const ra_tensor& dv_acc, hipStream_t s) {
+    if (q.S == 0 || k.S == 0) return hipSuccess;
+    const int rpb = kThreads / (q.D / kSub);
+    dim3 g((k.S + rpb - 1) / rpb, k.H, k.B);
+    if (q.D == 64) bwd_dkdv_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
+    else bwd_dkdv_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
     return hipGetLastError();
 }
 

@@ -230,11 +230,40 @@ ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_ten
     return RA_OK;
 }
 
+ra_status enqueue_bwd_dkdv(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                           const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk,
+                           const ra_tensor& dv, hipStream_t s) {
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dkdv_bf16(q, k, v, dout, lse, delta, scale, dk, dv, s));
+    else RA_HIP(ra::launch_bwd_dkdv_f32(q, k, v, dout, lse, delta, scale, dk, dv, s));
+    return RA_OK;
+}
+
+ra_status enqueue_bwd_dq(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
+                         const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq, hipStream_t s) {
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dq_bf16(q, k, v, dout, lse, delta, scale, dq, s));
+    else RA_HIP(ra::launch_bwd_dq_f32(q, k, v, dout, lse, delta, scale, dq, s));
+    return RA_OK;
+}
+
 ra_status enqueue_bwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                             const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq,
                             const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_chunk_bf16(q, k, v, dout, lse, delta, scale, dq, dk, dv, s));
-    else RA_HIP(ra::launch_bwd_chunk_f32(q, k, v, dout, lse, delta, scale, dq, dk, dv, s));
+    RA_TRY(enqueue_bwd_dkdv(q, k, v, dout, lse, delta, scale, dk, dv, s));
+    RA_TRY(enqueue_bwd_dq(q, k, v, dout, lse, delta, scale, dq, s));
+    return RA_OK;
+}
+
+// Shared validation of the backward chunk entry points (accumulators may be NULL when
+// the entry point does not touch them).
+ra_status check_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                          const ra_lse* lse, const ra_lse* delta, float scale) {
+    RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_tensor(dout, "dout"));
+    if (dout->dtype != q->dtype) return fail(RA_E_DTYPE, "dout must have the dtype of q");
+    if (!same_shape(*dout, *q)) return fail(RA_E_SHAPE, "dout must have the shape of q");
+    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
+    RA_TRY(check_rows(delta, "delta", q->B, q->H, q->S));
+    RA_TRY(check_scale(scale));
     return RA_OK;
 }
 
@@ -278,12 +307,7 @@ ra_status ra_bwd_delta(const ra_tensor* out, const ra_tensor* dout, ra_lse* delt
 ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
                        const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, ra_tensor* dk_acc,
                        ra_tensor* dv_acc, int32_t accumulate, void* stream) {
-    RA_TRY(check_qkv(q, k, v));
-    RA_TRY(check_tensor(dout, "dout"));
-    if (dout->dtype != q->dtype || !same_shape(*dout, *q)) return fail(RA_E_SHAPE, "dout must match q in shape and dtype");
-    RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
-    RA_TRY(check_rows(delta, "delta", q->B, q->H, q->S));
-    RA_TRY(check_scale(scale));
+    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
     RA_TRY(check_acc(dq_acc, "dq_acc", *q));
     RA_TRY(check_acc(dk_acc, "dk_acc", *k));
     RA_TRY(check_acc(dv_acc, "dv_acc", *k));
@@ -294,6 +318,30 @@ ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* 
         RA_HIP(ra::launch_zero_f32(*dv_acc, s));
     }
     if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_chunk(*q, *k, *v, *dout, *lse, *delta, scale, *dq_acc, *dk_acc, *dv_acc, s));
+    return ok();
+}
+
+ra_status ra_bwd_chunk_dkdv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                            const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dk_acc,
+                            ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
+    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
+    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
+    if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate) {
+        RA_HIP(ra::launch_zero_f32(*dk_acc, s));
+        RA_HIP(ra::launch_zero_f32(*dv_acc, s));
+    }
+    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_dkdv(*q, *k, *v, *dout, *lse, *delta, scale, *dk_acc, *dv_acc, s));
+    return ok();
+}
+
+ra_status ra_bwd_chunk_dq(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                          const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, void* stream) {
+    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
+    RA_TRY(check_acc(dq_acc, "dq_acc", *q));
+    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_dq(*q, *k, *v, *dout, *lse, *delta, scale, *dq_acc, (hipStream_t)stream));
     return ok();
 }
 

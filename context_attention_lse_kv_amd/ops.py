@@ -117,6 +117,21 @@ def bwd_chunk(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, accumulate, sca
                              a[0], a[1], a[2], int(accumulate), _stream(q)), "ra_bwd_chunk")
 
 
+def bwd_chunk_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, accumulate, scale=None, layout="bshd"):
+    _dev_check(q, k, v, dout, lse, delta, dk_acc, dv_acc)
+    d = [tensor_desc(x, layout) for x in (q, k, v, dout, dk_acc, dv_acc)]
+    check(lib().ra_bwd_chunk_dkdv(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
+                                  _scale(scale, q.shape[-1]), d[4], d[5], int(accumulate), _stream(q)),
+          "ra_bwd_chunk_dkdv")
+
+
+def bwd_chunk_dq(q, k, v, dout, lse, delta, dq_acc, scale=None, layout="bshd"):
+    _dev_check(q, k, v, dout, lse, delta, dq_acc)
+    d = [tensor_desc(x, layout) for x in (q, k, v, dout, dq_acc)]
+    check(lib().ra_bwd_chunk_dq(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
+                                _scale(scale, q.shape[-1]), d[4], _stream(q)), "ra_bwd_chunk_dq")
+
+
 def _rows_shape(q, layout):
     if layout == "bshd":
         B, S, H, _ = q.shape

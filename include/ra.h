@@ -140,6 +140,19 @@ ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* 
                        float scale, ra_tensor* dq_acc, ra_tensor* dk_acc, ra_tensor* dv_acc,
                        int32_t accumulate, void* stream);
 
+/* The two halves of ra_bwd_chunk, for callers that schedule them separately (in a
+ * ring, a step's dK/dV leave the rank while its dQ contribution stays local).
+ * Same arguments and rules as ra_bwd_chunk; ra_bwd_chunk_dkdv touches only dk_acc
+ * and dv_acc (accumulate = 0 overwrites, 1 adds), ra_bwd_chunk_dq only adds to
+ * dq_acc. */
+ra_status ra_bwd_chunk_dkdv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                            const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                            float scale, ra_tensor* dk_acc, ra_tensor* dv_acc,
+                            int32_t accumulate, void* stream);
+ra_status ra_bwd_chunk_dq(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                          const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                          float scale, ra_tensor* dq_acc, void* stream);
+
 /* ---------------------------------------------------------------- ring sweeps */
 
 /* Forward sweep of the local query shard over every chunk in chunks->order:

@@ -333,6 +333,32 @@ def test_fwd_chunk_and_merge_lse():
     assert torch.all(z_o == 0) and torch.all(torch.isneginf(z_l))
 
 
+def test_bwd_chunk_halves_match_whole_step():
+    """ra_bwd_chunk_dkdv + ra_bwd_chunk_dq reproduce ra_bwd_chunk, and each matches the
+    oracle's gradients of a one-chunk sweep (bf16 and fp32 paths, GQA, odd sizes)."""
+    d = dev()
+    for dt, tol in (("bf16", BF16_TOL), ("f32", F32_TOL)):
+        B, Sq, Sk, Hq, Hkv, D = 1, 150, 203, 4, 2, 128
+        q = W.randn((B, Sq, Hq, D), 40, dt); k = W.randn((B, Sk, Hkv, D), 41, dt)
+        v = W.randn((B, Sk, Hkv, D), 42, dt); do = W.randn((B, Sq, Hq, D), 43, dt)
+        gq, gk, gv, gdo = to_dev(q, k, v, do)
+        out, lse = ra.ring_fwd(gq, gk, gv, ra.Chunks([Sk]), out_dtype=torch.float32)
+        delta = torch.empty_like(lse)
+        ra.bwd_delta(out, gdo, delta)
+        z = lambda t: torch.zeros(t.shape, dtype=torch.float32, device=d)
+        dq1, dk1, dv1 = z(gq), z(gk), z(gk)
+        ra.bwd_chunk(gq, gk, gv, gdo, lse, delta, dq1, dk1, dv1, accumulate=0)
+        dq2, dk2, dv2 = z(gq), z(gk), z(gk)
+        ra.bwd_chunk_dkdv(gq, gk, gv, gdo, lse, delta, dk2, dv2, accumulate=0)
+        ra.bwd_chunk_dq(gq, gk, gv, gdo, lse, delta, dq2)
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, dq2)  # same kernel, single writer per row: bit-identical
+        assert rel(np64(dk1), np64(dk2)) <= 1e-6 and rel(np64(dv1), np64(dv2)) <= 1e-6  # atomics reorder sums
+        ref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(do))
+        for got, r in zip((dq2, dk2, dv2), ref):
+            assert rel(np64(got), r) <= tol
+
+
 def test_bwd_delta_against_oracle():
     d = dev()
     for odt, ddt in ((torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16), (torch.float32, torch.float32)):

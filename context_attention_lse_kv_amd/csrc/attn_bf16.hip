@@ -472,49 +472,65 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* qb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* ob = lbase + (2 * buf + 1) * TILEB;
+        // Software pipeline over the tile's row blocks: the operand reads of each MFMA
+        // group are issued together ahead of the group, and the softmax VALU work of one
+        // row block sits next to the MFMAs of the other so the two can overlap.
+        f32x16_t sacc[RB], dpacc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            f32x16_t sacc = f32x16_t{}, dpacc = f32x16_t{};
+            bf16x8_t qa[KS], oa[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                sacc = mfma32(lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks])), kreg[ks], sacc);
-                dpacc = mfma32(lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks])), vreg[ks], dpacc);
+                qa[ks] = lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks]));
+                oa[ks] = lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks]));
             }
+            sacc[rb] = f32x16_t{};
+            dpacc[rb] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                sacc[rb] = mfma32(qa[ks], kreg[ks], sacc[rb]);
+                dpacc[rb] = mfma32(oa[ks], vreg[ks], dpacc[rb]);
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
             // lane = key, register r = row 32*rb + 8*(r/4) + 4*hh + r%4
-            float pv[16], dsv[16];
+            u32x4_t pp[2], pd[2];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const f32x4_t l2 = *(const RA_LDS f32x4_t*)&stat[buf][0][32 * rb + 8 * g4 + 4 * hh];
                 const f32x4_t dl = *(const RA_LDS f32x4_t*)&stat[buf][1][32 * rb + 8 * g4 + 4 * hh];
+                float pv[4], dsv[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pv[4 * g4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g4 + j], p.c, -l2[j]));
-                if (keys_partial) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) pv[4 * g4 + j] = key_ok ? pv[4 * g4 + j] : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));
+                    if (keys_partial) pv[j] = key_ok ? pv[j] : 0.f;
+                    dsv[j] = pv[j] * (dpacc[rb][4 * g4 + j] - dl[j]);
                 }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dsv[4 * g4 + j] = pv[4 * g4 + j] * (dpacc[4 * g4 + j] - dl[j]);
+                pp[g4 / 2][2 * (g4 % 2)] = pack_bf16x2(pv[0], pv[1]);
+                pp[g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
+                pd[g4 / 2][2 * (g4 % 2)] = pack_bf16x2(dsv[0], dsv[1]);
+                pd[g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(dsv[2], dsv[3]);
             }
             // dV += P^T dO, dK += dS^T Q (k = query rows, 2 k-steps of 16)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-                u32x4_t pp, pd;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pp[j] = pack_bf16x2(pv[8 * t2 + 2 * j], pv[8 * t2 + 2 * j + 1]);
-                    pd[j] = pack_bf16x2(dsv[8 * t2 + 2 * j], dsv[8 * t2 + 2 * j + 1]);
-                }
-                const bf16x8_t pa = as_bf16x8(pp), da = as_bf16x8(pd);
                 const int roff = (32 * rb + 16 * t2) * ROWB;
+                u32x2_t ot[DB][2], qt[DB][2];
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const u32x2_t o0 = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
-                    const u32x2_t o1 = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off[db]));
-                    dvacc[db] = mfma32(pa, as_bf16x8(u32x4_t{o0[0], o0[1], o1[0], o1[1]}), dvacc[db]);
-                    const u32x2_t q0 = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
-                    const u32x2_t q1 = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off[db]));
-                    dkacc[db] = mfma32(da, as_bf16x8(u32x4_t{q0[0], q0[1], q1[0], q1[1]}), dkacc[db]);
+                    ot[db][0] = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
+                    ot[db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off[db]));
+                    qt[db][0] = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
+                    qt[db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off[db]));
+                }
+                const bf16x8_t pa = as_bf16x8(pp[t2]), da = as_bf16x8(pd[t2]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dvacc[db] = mfma32(pa, as_bf16x8(u32x4_t{ot[db][0][0], ot[db][0][1], ot[db][1][0], ot[db][1][1]}),
+                                       dvacc[db]);
+                    dkacc[db] = mfma32(da, as_bf16x8(u32x4_t{qt[db][0][0], qt[db][0][1], qt[db][1][0], qt[db][1][1]}),
+                                       dkacc[db]);
                 }
             }
         }

@@ -313,11 +313,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 }
 
 // ============================================================================ backward
-// Row swizzle of the unpadded Q / dO / K tiles in LDS: 16-byte chunk c of tile row r
-// lives at chunk slot c ^ swz(r).  Eight consecutive rows (the 16-byte row reads of an
-// MFMA operand) and the 4 rows x 2 chunks of a transposing read then fall on distinct
-// bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Row swizzle of the unpadded Q / dO / K / V tiles in LDS: 16-byte chunk c of tile row
+// r lives at chunk slot c ^ swz<RC>(r) (RC = chunks per row).  Consecutive rows (the
+// 16-byte row reads of an MFMA operand) and the 4 rows x 2..4 chunks of transposing
+// reads then fall on distinct bank groups.
+template <int RC>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (RC >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return ((r & 3) << 1) | ((r >> 2) & 1);
+}
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
@@ -361,7 +365,7 @@ template <int D>
 __device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
     constexpr int RC = D / 8, RPI = 1024 / (D * 2);
     const int r = ci * RPI + lane / RC;
-    const int c = (lane % RC) ^ swz(r);
+    const int c = (lane % RC) ^ swz<RC>(r);
     return (uint32_t)((r * sS + 8 * c) * 2);
 }
 
@@ -393,7 +397,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
     const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
     const int n0 = kt * BN;
     const int key = n0 + 32 * w + l32;  // this lane's key (column of S/dP, row of dK/dV)
-    const bool key_ok = key < p.Sk;
     const bool keys_partial = n0 + BN > p.Sk;
 
     const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
@@ -451,15 +454,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         dvacc[db] = f32x16_t{};
     }
     // lane-constant LDS offsets: row reads (S, dP operands) and transposing reads (dV, dK)
-    const int sw_row = swz(l32);
+    const int sw_row = swz<RC>(l32);
     int ra_off[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
-    const int sw_tr = swz(4 * hh + e4);
-    int tr_off[DB];
+    const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
+    int tr_off[DB], tr_off8[DB];  // transposing reads of rows r and r + 8
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
         tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+        tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
+    }
 
     issue(0, 0);
     wait_vmem();
@@ -472,24 +477,30 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* qb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* ob = lbase + (2 * buf + 1) * TILEB;
-        // Software pipeline over the tile's row blocks: the operand reads of each MFMA
-        // group are issued together ahead of the group, and the softmax VALU work of one
-        // row block sits next to the MFMAs of the other so the two can overlap.
+        // S and dP of both row blocks; operand reads kept PF MFMA pairs ahead.  Keys past
+        // the chunk (K = V = 0 there) need no mask: their P and dS only reach their own
+        // rows of the dK/dV accumulators, which are never stored.
+        constexpr int NS = RB * KS, PF = 4;
         f32x16_t sacc[RB], dpacc[RB];
+        bf16x8_t stq[PF], sto[PF];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            bf16x8_t qa[KS], oa[KS];
+        for (int i = 0; i < PF; ++i) {
+            stq[i] = lds_b128((const lds_u16*)(qb + 32 * (i / KS) * ROWB + ra_off[i % KS]));
+            sto[i] = lds_b128((const lds_u16*)(ob + 32 * (i / KS) * ROWB + ra_off[i % KS]));
+        }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qa[ks] = lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks]));
-                oa[ks] = lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks]));
+        for (int i = 0; i < NS; ++i) {
+            const int rb = i / KS, ks = i % KS;
+            if (ks == 0) {
+                sacc[rb] = f32x16_t{};
+                dpacc[rb] = f32x16_t{};
             }
-            sacc[rb] = f32x16_t{};
-            dpacc[rb] = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sacc[rb] = mfma32(qa[ks], kreg[ks], sacc[rb]);
-                dpacc[rb] = mfma32(oa[ks], vreg[ks], dpacc[rb]);
+            sacc[rb] = mfma32(stq[i % PF], kreg[ks], sacc[rb]);
+            dpacc[rb] = mfma32(sto[i % PF], vreg[ks], dpacc[rb]);
+            if (i + PF < NS) {
+                const int rn = (i + PF) / KS, kn = (i + PF) % KS;
+                stq[i % PF] = lds_b128((const lds_u16*)(qb + 32 * rn * ROWB + ra_off[kn]));
+                sto[i % PF] = lds_b128((const lds_u16*)(ob + 32 * rn * ROWB + ra_off[kn]));
             }
         }
 #pragma unroll
@@ -504,7 +515,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));
-                    if (keys_partial) pv[j] = key_ok ? pv[j] : 0.f;
                     dsv[j] = pv[j] * (dpacc[rb][4 * g4 + j] - dl[j]);
                 }
                 pp[g4 / 2][2 * (g4 % 2)] = pack_bf16x2(pv[0], pv[1]);
@@ -520,9 +530,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     ot[db][0] = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
-                    ot[db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off[db]));
+                    ot[db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off8[db]));
                     qt[db][0] = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
-                    qt[db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off[db]));
+                    qt[db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off8[db]));
                 }
                 const bf16x8_t pa = as_bf16x8(pp[t2]), da = as_bf16x8(pd[t2]);
 #pragma unroll
@@ -617,15 +627,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
             dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
         }
     };
-    const int sw_row = swz(l32);
+    const int sw_row = swz<RC>(l32);
     int ra_off[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
-    const int sw_tr = swz(4 * hh + e4);
-    int tr_off[DB];
+    const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
+    int tr_off[DB], tr_off8[DB];  // transposing reads of rows r and r + 8
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
         tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+        tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
+    }
 
     f32x16_t dqacc[DB];
 #pragma unroll
@@ -677,7 +689,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const u32x2_t k0 = lds_tr((const lds_u16*)(kb + 16 * t * ROWB + tr_off[db]));
-                const u32x2_t k1 = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off[db]));
+                const u32x2_t k1 = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off8[db]));
                 dqacc[db] = mfma32(as_bf16x8(u32x4_t{k0[0], k0[1], k1[0], k1[1]}), bds, dqacc[db]);
             }
         }

@@ -28,10 +28,10 @@
 // The recompute of S and dP in both kernels (7 products instead of 5) is cheaper on
 // this chip than adding dQ through device-scope atomics from every key tile.
 //
-// Both kernels stream their tiles with buffer loads (rows past the end of a
-// slice read as zeros, so tails need no branches), keep the next tile in
-// registers while the current one is computed, and double-buffer the LDS tiles
-// so that one barrier per tile suffices.
+// All kernels stream their tiles HBM -> LDS with buffer->LDS copies (rows past the
+// end of a slice arrive as zeros, so tails need no branches), into unpadded rows with
+// an XOR swizzle of 16-byte chunks, double-buffered so that the next tile is in
+// flight while the current one is computed and one barrier per tile suffices.
 #include "ra_device.h"
 
 #define RA_LDS __attribute__((address_space(3)))
@@ -108,211 +108,10 @@ __device__ __forceinline__ u32x2_t lds_tr(const lds_u16* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-// MFMA operand of 8 bf16 made of rows r0..r0+3 and r0+8..r0+11 of column (c0 + lane)
-// of a row-major LDS tile (pitch P): the k order of a 32x32 accumulator reused as an
-// operand.  `p` already points at row r0 + e, column c0 + 4a of this lane.
-template <int P>
-__device__ __forceinline__ bf16x8_t lds_tr_split8(const lds_u16* p) {
-    const u32x2_t lo = lds_tr(p), hi = lds_tr(p + 8 * P);
-    return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-}
-// Same with 8 consecutive rows r0..r0+7.
-template <int P>
-__device__ __forceinline__ bf16x8_t lds_tr_cont8(const lds_u16* p) {
-    const u32x2_t lo = lds_tr(p), hi = lds_tr(p + 4 * P);
-    return as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-}
-
 inline uint32_t span_bytes(int rows, int64_t stride, int D) {
     return rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * stride + D) * 2);
 }
 
-// ============================================================================ forward
-template <int D, bool MERGE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
-    constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
-    constexpr int KP = D + 8;    // K tile pitch (16-byte row reads)
-    constexpr int VP = D + 16;   // V tile pitch (transposing reads)
-    constexpr int KT = BN * KP, VT = BN * VP;
-    constexpr int CH = BN * (D / 8) / 256;  // 16-byte chunks per thread per tile
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
-    lds_u16* const Ks = (lds_u16*)smem;
-    lds_u16* const Vs = Ks + 2 * KT;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int gq = lane >> 4, l16 = lane & 15;
-    const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt = (int)(logical % p.n_qtiles);
-    const int rest = (int)(logical / p.n_qtiles);
-    const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
-    const int row = qt * BM + w * 32 + l32;
-    const bool row_ok = row < p.Sq;
-
-    bf16x8_t qreg[KS];
-    {
-        const uint16_t* qrow = p.q + (int64_t)b * p.q_sB + (int64_t)row * p.q_sS + (int64_t)h * p.q_sH;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qreg[ks] = row_ok ? as_bf16x8(*(const u32x4_t*)(qrow + 16 * ks + 8 * hh))
-                              : as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
-    }
-    f32x16_t oacc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
-    float m = -INFINITY, l = 0.f;
-
-    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
-    const uint16_t* vbase = p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
-    uint32_t vk[CH], vv[CH];
-    int ko[CH], vo[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int c = tid + 256 * j, r = c / (D / 8), c8 = c % (D / 8);
-        vk[j] = (uint32_t)((r * p.k_sS + 8 * c8) * 2);
-        vv[j] = (uint32_t)((r * p.v_sS + 8 * c8) * 2);
-        ko[j] = r * KP + 8 * c8;
-        vo[j] = r * VP + 8 * c8;
-    }
-    u32x4_t kpre[CH], vpre[CH];
-    // lane-constant parts of the transposing-read addresses of V
-    const int vtr = (4 * hh + (l16 >> 2)) * VP + 16 * (gq & 1) + 4 * (l16 & 3);
-
-    {
-        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, 0, p.k_sS * 2, p.k_bytes);
-        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, 0, p.v_sS * 2, p.v_bytes);
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            kpre[j] = bload16(rk, vk[j], 0);
-            vpre[j] = bload16(rv, vv[j], 0);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        *(RA_LDS u32x4_t*)(Ks + ko[j]) = kpre[j];
-        *(RA_LDS u32x4_t*)(Vs + vo[j]) = vpre[j];
-    }
-    __syncthreads();
-
-    const int ntiles = (p.Sk + BN - 1) / BN;
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1, n0 = it * BN;
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, n0 + BN, p.k_sS * 2, p.k_bytes);
-            const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, n0 + BN, p.v_sS * 2, p.v_bytes);
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                kpre[j] = bload16(rk, vk[j], 0);
-                vpre[j] = bload16(rv, vv[j], 0);
-            }
-        }
-        const lds_u16* kb = Ks + buf * KT;
-        const lds_u16* vb = Vs + buf * VT;
-
-        // S^T (keys x rows) for this wave's 32 rows: two 32-key blocks
-        f32x16_t sacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            sacc[kb2] = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc[kb2] = mfma32(lds_b128(kb + (kb2 * 32 + l32) * KP + 16 * ks + 8 * hh), qreg[ks], sacc[kb2]);
-        }
-        if (n0 + BN > p.Sk) {  // last tile: keys past the chunk read as zero; mask them
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
-        }
-        // online softmax in base 2 on t = s * scale * log2(e), with a lazily moved max
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-        mx = fmaxf(mx, swap_half(mx)) * p.c;
-        if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m = m_new;
-        }
-        u32x4_t pk[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 8 * (t % 2) + 2 * j;
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -m));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -m));
-                l += p0 + p1;
-                pk[t][j] = pack_bf16x2(p0, p1);
-            }
-        // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16x8_t pb = as_bf16x8(pk[t]);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                oacc[db] = mfma32(lds_tr_split8<VP>(vb + vtr + 16 * t * VP + 32 * db), pb, oacc[db]);
-        }
-        if (more) {
-            lds_u16* kn = Ks + (buf ^ 1) * KT;
-            lds_u16* vn = Vs + (buf ^ 1) * VT;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                *(RA_LDS u32x4_t*)(kn + ko[j]) = kpre[j];
-                *(RA_LDS u32x4_t*)(vn + vo[j]) = vpre[j];
-            }
-        }
-        __syncthreads();
-    }
-
-    l += swap_half(l);
-    if (!row_ok) return;
-    const float inv_l = 1.f / l;
-    const float lse_c = m * kLn2 + logf(l);
-    float* orow = p.out + (int64_t)b * p.o_sB + (int64_t)row * p.o_sS + (int64_t)h * p.o_sH;
-    float* lp = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row;
-    if (!MERGE) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4_t v4 = {oacc[db][4 * g4] * inv_l, oacc[db][4 * g4 + 1] * inv_l,
-                                    oacc[db][4 * g4 + 2] * inv_l, oacc[db][4 * g4 + 3] * inv_l};
-                *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = v4;
-            }
-        if (hh == 0) *lp = lse_c;
-    } else {
-        // both lanes of the row (l and l^32) read lse_acc before lane l writes it (same wavefront)
-        const float la = *lp;
-        const float mm = fmaxf(la, lse_c);
-        const float ea = expf(la - mm), ec = expf(lse_c - mm);
-        const float sum = ea + ec;
-        const float wa = ea / sum, wc = ec / sum * inv_l;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4_t* po = (f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh);
-                const f32x4_t old = *po;
-                f32x4_t v4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (wa == 0.f ? 0.f : wa * old[j]) + wc * oacc[db][4 * g4 + j];
-                *po = v4;
-            }
-        if (hh == 0) *lp = mm + logf(sum);
-    }
-}
-
-// ============================================================================ backward
 // Row swizzle of the unpadded Q / dO / K / V tiles in LDS: 16-byte chunk c of tile row
 // r lives at chunk slot c ^ swz<RC>(r) (RC = chunks per row).  Consecutive rows (the
 // 16-byte row reads of an MFMA operand) and the 4 rows x 2..4 chunks of transposing
@@ -369,6 +168,183 @@ __device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
     return (uint32_t)((r * sS + 8 * c) * 2);
 }
 
+// ============================================================================ forward
+template <int D, bool MERGE>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
+    constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
+    constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
+    constexpr int RPI = 1024 / ROWB, NI = BN / RPI / 4;
+    static_assert(RC >= 8 && NI >= 1, "tile geometry");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [K0 | V0 | K1 | V1]
+    RA_LDS char* const lbase = (RA_LDS char*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int gq = lane >> 4, l16 = lane & 15, e4 = l16 >> 2, a4 = l16 & 3;
+    const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = (int)(logical % p.n_qtiles);
+    const int rest = (int)(logical / p.n_qtiles);
+    const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
+    const int row = qt * BM + w * 32 + l32;
+    const bool row_ok = row < p.Sq;
+
+    bf16x8_t qreg[KS];
+    {
+        const uint16_t* qrow = p.q + (int64_t)b * p.q_sB + (int64_t)row * p.q_sS + (int64_t)h * p.q_sH;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qreg[ks] = row_ok ? as_bf16x8(*(const u32x4_t*)(qrow + 16 * ks + 8 * hh))
+                              : as_bf16x8(u32x4_t{0u, 0u, 0u, 0u});
+    }
+    f32x16_t oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16_t{};
+    float m = -INFINITY, l = 0.f;
+
+    // K/V tiles stream HBM -> LDS (swizzled rows); keys past the chunk arrive as zeros
+    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
+    const uint16_t* vbase = p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
+    uint32_t vk[NI], vv[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        vk[i] = copy_voff<D>(w * NI + i, lane, p.k_sS);
+        vv[i] = copy_voff<D>(w * NI + i, lane, p.v_sS);
+    }
+    auto issue = [&](int it, int buf) {
+        const int r0 = it * BN;
+        const i32x4_t rk = tile_desc(kbase, r0, p.k_sS * 2, p.k_bytes);
+        const i32x4_t rv = tile_desc(vbase, r0, p.v_sS * 2, p.v_bytes);
+        RA_LDS char* kdst = lbase + (2 * buf) * TILEB;
+        RA_LDS char* vdst = lbase + (2 * buf + 1) * TILEB;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
+            dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
+        }
+    };
+    // lane-constant LDS offsets: K row reads (S^T operand) and transposing V reads (V^T operand)
+    const int sw_row = swz<RC>(l32);
+    int ra_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
+    const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
+    int tr_off[DB], tr_off8[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+        tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
+    }
+
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    const int ntiles = (p.Sk + BN - 1) / BN;
+    for (int it = 0; it < ntiles; ++it) {
+        const int buf = it & 1, n0 = it * BN;
+        const bool more = it + 1 < ntiles;
+        if (more) issue(it + 1, buf ^ 1);
+        const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
+        const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
+
+        // S^T (keys x rows) for this wave's 32 rows: two 32-key blocks
+        f32x16_t sacc[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            sacc[kb2] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[kb2] = mfma32(lds_b128((const lds_u16*)(kb + kb2 * 32 * ROWB + ra_off[ks])), qreg[ks], sacc[kb2]);
+        }
+        if (n0 + BN > p.Sk) {  // last tile: keys past the chunk read as zero; mask them
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
+        }
+        // online softmax in base 2 on t = s * scale * log2(e), with a lazily moved max
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
+        mx = fmaxf(mx, swap_half(mx)) * p.c;
+        if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m = m_new;
+        }
+        u32x4_t pk[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 8 * (t % 2) + 2 * j;
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -m));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -m));
+                l += p0 + p1;
+                pk[t][j] = pack_bf16x2(p0, p1);
+            }
+        // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8_t pb = as_bf16x8(pk[t]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const u32x2_t v0 = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
+                const u32x2_t v1 = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
+                oacc[db] = mfma32(as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]}), pb, oacc[db]);
+            }
+        }
+        if (more) wait_vmem();
+        __syncthreads();
+    }
+
+    l += swap_half(l);
+    if (!row_ok) return;
+    const float inv_l = 1.f / l;
+    const float lse_c = m * kLn2 + logf(l);
+    float* orow = p.out + (int64_t)b * p.o_sB + (int64_t)row * p.o_sS + (int64_t)h * p.o_sH;
+    float* lp = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row;
+    if (!MERGE) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4_t v4 = {oacc[db][4 * g4] * inv_l, oacc[db][4 * g4 + 1] * inv_l,
+                                    oacc[db][4 * g4 + 2] * inv_l, oacc[db][4 * g4 + 3] * inv_l};
+                *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = v4;
+            }
+        if (hh == 0) *lp = lse_c;
+    } else {
+        // both lanes of the row (l and l^32) read lse_acc before lane l writes it (same wavefront)
+        const float la = *lp;
+        const float mm = fmaxf(la, lse_c);
+        const float ea = expf(la - mm), ec = expf(lse_c - mm);
+        const float sum = ea + ec;
+        const float wa = ea / sum, wc = ec / sum * inv_l;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4_t* po = (f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh);
+                const f32x4_t old = *po;
+                f32x4_t v4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[j] = (wa == 0.f ? 0.f : wa * old[j]) + wc * oacc[db][4 * g4 + j];
+                *po = v4;
+            }
+        if (hh == 0) *lp = mm + logf(sum);
+    }
+}
+
+// ============================================================================ backward
 // --------------------------------------------------------------- dK, dV (KV-stationary)
 // Workgroup = 128 keys of the chunk (32 per wavefront) x one query head; sweeps every
 // query row of that head in tiles of 64.  No dQ here (see bwd_dq_bf16_kernel), so the

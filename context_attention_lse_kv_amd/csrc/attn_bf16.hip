@@ -446,6 +446,18 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
     wait_vmem();
     commit_stats(0);
     __syncthreads();
+    // One Q tile is a software pipeline of slots holding two MFMAs each: slots [0, NS)
+    // compute S and dP of row block rb = s / KS at k-step s % KS, slots [NS, NSLOT) add
+    // dV and dK of group g = (rb, t2) (16 query rows) and column block db.  Operand
+    // reads are issued PF (row reads) or LT (transposing reads) slots before their
+    // MFMAs; the softmax of a row block runs in the slots after its last S/dP MFMA, its
+    // statistics read one slot earlier.  A scheduling barrier closes every slot, so
+    // the compiler cannot sink a read next to its consumer.
+    //   Keys past the chunk (K = V = 0 there) need no mask: their P and dS only reach
+    // their own rows of the dK/dV accumulators, which are never stored.
+    constexpr int NS = RB * KS, NG = 2 * RB, NSLOT = NS + NG * DB;
+    constexpr int PF = 4, LT = DB < 2 ? DB : 2;
+    static_assert(LT <= DB, "transposing reads must not overwrite operands still in use");
     const int ntiles = (p.Sq + BM - 1) / BM;
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
@@ -453,72 +465,75 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* qb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* ob = lbase + (2 * buf + 1) * TILEB;
-        // S and dP of both row blocks; operand reads kept PF MFMA pairs ahead.  Keys past
-        // the chunk (K = V = 0 there) need no mask: their P and dS only reach their own
-        // rows of the dK/dV accumulators, which are never stored.
-        constexpr int NS = RB * KS, PF = 4;
         f32x16_t sacc[RB], dpacc[RB];
         bf16x8_t stq[PF], sto[PF];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            stq[i] = lds_b128((const lds_u16*)(qb + 32 * (i / KS) * ROWB + ra_off[i % KS]));
-            sto[i] = lds_b128((const lds_u16*)(ob + 32 * (i / KS) * ROWB + ra_off[i % KS]));
-        }
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
+        u32x4_t pp[RB][2], pd[RB][2];       // P and dS as bf16 MFMA A-operands, per (rb, t2)
+        u32x2_t tro[2][DB][2], trq[2][DB][2];
+        f32x4_t sl2[2], sdl[2];
+
+        auto row_read = [&](int i) {
             const int rb = i / KS, ks = i % KS;
-            if (ks == 0) {
-                sacc[rb] = f32x16_t{};
-                dpacc[rb] = f32x16_t{};
+            stq[i % PF] = lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks]));
+            sto[i % PF] = lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks]));
+        };
+        auto tr_read = [&](int grp) {  // dO^T and Q^T operands of query rows 16 grp .. 16 grp + 15
+            const int roff = 16 * grp * ROWB, pb = grp & 1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                tro[pb][db][0] = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
+                tro[pb][db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off8[db]));
+                trq[pb][db][0] = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
+                trq[pb][db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off8[db]));
             }
-            sacc[rb] = mfma32(stq[i % PF], kreg[ks], sacc[rb]);
-            dpacc[rb] = mfma32(sto[i % PF], vreg[ks], dpacc[rb]);
-            if (i + PF < NS) {
-                const int rn = (i + PF) / KS, kn = (i + PF) % KS;
-                stq[i % PF] = lds_b128((const lds_u16*)(qb + 32 * rn * ROWB + ra_off[kn]));
-                sto[i % PF] = lds_b128((const lds_u16*)(ob + 32 * rn * ROWB + ra_off[kn]));
+        };
+        auto stat_read = [&](int rb, int g4) {
+            const int r = 32 * rb + 8 * g4 + 4 * hh;
+            sl2[g4 & 1] = *(const RA_LDS f32x4_t*)&stat[buf][0][r];
+            sdl[g4 & 1] = *(const RA_LDS f32x4_t*)&stat[buf][1][r];
+        };
+        // lane = key, register 4 g4 + j = query row 32 rb + 8 g4 + 4 hh + j
+        auto softmax = [&](int rb, int g4) {
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -sl2[g4 & 1][j]));
+                dsv[j] = pv[j] * (dpacc[rb][4 * g4 + j] - sdl[g4 & 1][j]);
             }
-        }
+            pp[rb][g4 / 2][2 * (g4 % 2)] = pack_bf16x2(pv[0], pv[1]);
+            pp[rb][g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
+            pd[rb][g4 / 2][2 * (g4 % 2)] = pack_bf16x2(dsv[0], dsv[1]);
+            pd[rb][g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        };
+
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            // lane = key, register r = row 32*rb + 8*(r/4) + 4*hh + r%4
-            u32x4_t pp[2], pd[2];
+        for (int i = 0; i < PF; ++i) row_read(i);
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4_t l2 = *(const RA_LDS f32x4_t*)&stat[buf][0][32 * rb + 8 * g4 + 4 * hh];
-                const f32x4_t dl = *(const RA_LDS f32x4_t*)&stat[buf][1][32 * rb + 8 * g4 + 4 * hh];
-                float pv[4], dsv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));
-                    dsv[j] = pv[j] * (dpacc[rb][4 * g4 + j] - dl[j]);
-                }
-                pp[g4 / 2][2 * (g4 % 2)] = pack_bf16x2(pv[0], pv[1]);
-                pp[g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
-                pd[g4 / 2][2 * (g4 % 2)] = pack_bf16x2(dsv[0], dsv[1]);
-                pd[g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        for (int s = 0; s < NSLOT; ++s) {
+            if (s < NS) {
+                const int rb = s / KS, ks = s % KS;
+                sacc[rb] = mfma32(stq[s % PF], kreg[ks], ks == 0 ? f32x16_t{} : sacc[rb]);
+                dpacc[rb] = mfma32(sto[s % PF], vreg[ks], ks == 0 ? f32x16_t{} : dpacc[rb]);
+                if (s + PF < NS) row_read(s + PF);
+            } else {
+                // dV += P^T dO, dK += dS^T Q over 16 query rows (one MFMA k-step)
+                const int grp = (s - NS) / DB, db = (s - NS) % DB, rb = grp / 2, t2 = grp % 2, pb = grp & 1;
+                dvacc[db] = mfma32(as_bf16x8(pp[rb][t2]),
+                                   as_bf16x8(u32x4_t{tro[pb][db][0][0], tro[pb][db][0][1], tro[pb][db][1][0], tro[pb][db][1][1]}),
+                                   dvacc[db]);
+                dkacc[db] = mfma32(as_bf16x8(pd[rb][t2]),
+                                   as_bf16x8(u32x4_t{trq[pb][db][0][0], trq[pb][db][0][1], trq[pb][db][1][0], trq[pb][db][1][1]}),
+                                   dkacc[db]);
             }
-            // dV += P^T dO, dK += dS^T Q (k = query rows, 2 k-steps of 16)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) {
-                const int roff = (32 * rb + 16 * t2) * ROWB;
-                u32x2_t ot[DB][2], qt[DB][2];
+            for (int grp = 0; grp < NG; ++grp)
+                if (s == NS + grp * DB - LT) tr_read(grp);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    ot[db][0] = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
-                    ot[db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off8[db]));
-                    qt[db][0] = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
-                    qt[db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off8[db]));
-                }
-                const bf16x8_t pa = as_bf16x8(pp[t2]), da = as_bf16x8(pd[t2]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dvacc[db] = mfma32(pa, as_bf16x8(u32x4_t{ot[db][0][0], ot[db][0][1], ot[db][1][0], ot[db][1][1]}),
-                                       dvacc[db]);
-                    dkacc[db] = mfma32(da, as_bf16x8(u32x4_t{qt[db][0][0], qt[db][0][1], qt[db][1][0], qt[db][1][1]}),
-                                       dkacc[db]);
-                }
+            for (int rb = 0; rb < RB; ++rb) {
+                const int s0 = (rb + 1) * KS + 1;  // two slots after the row block's last S/dP MFMA
+                if (s >= s0 - 1 && s < s0 + 3) stat_read(rb, s - s0 + 1);
+                if (s >= s0 && s < s0 + 4) softmax(rb, s - s0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) {
             wait_vmem();

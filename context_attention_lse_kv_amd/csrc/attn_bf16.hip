@@ -239,50 +239,54 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     issue(0, 0);
     wait_vmem();
     __syncthreads();
+    // One key tile is a software pipeline of single-MFMA slots: slots [0, NSS) compute
+    // S^T of key block kb2 = s / KS at k-step s % KS, slots [NSS, NSLOT) add V^T P^T for
+    // 16 keys t and column block db.  Row reads run PF slots and transposing reads LT
+    // slots ahead of their MFMAs; each 32-key block gets its own max and exponentials two
+    // slots after its last S^T MFMA, so the softmax of block 0 overlaps the MFMAs of
+    // block 1 and that of block 1 the first P V MFMAs.  A scheduling barrier closes
+    // every slot.
+    //   The running max moves lazily (only when a block exceeds it by more than
+    // kRescale, in log2 units).  A move triggered by block 1 rescales l at once but the
+    // O accumulator only after the P V MFMAs of block 0, which still use the old max.
+    constexpr int NSS = 2 * KS, NSLOT = NSS + 4 * DB;
+    constexpr int PF = 4, LT = 2;
     const int ntiles = (p.Sk + BN - 1) / BN;
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1, n0 = it * BN;
         const bool more = it + 1 < ntiles;
+        const bool last = n0 + BN > p.Sk;
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
-
-        // S^T (keys x rows) for this wave's 32 rows: two 32-key blocks
         f32x16_t sacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            sacc[kb2] = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc[kb2] = mfma32(lds_b128((const lds_u16*)(kb + kb2 * 32 * ROWB + ra_off[ks])), qreg[ks], sacc[kb2]);
-        }
-        if (n0 + BN > p.Sk) {  // last tile: keys past the chunk read as zero; mask them
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+        bf16x8_t stk[NSS];
+        u32x4_t pk[4];
+        u32x2_t trv[4 * DB][2];
+        float alpha1 = 1.f;
+        bool late = false;
+
+        auto row_read = [&](int i) {
+            stk[i] = lds_b128((const lds_u16*)(kb + (i / KS) * 32 * ROWB + ra_off[i % KS]));
+        };
+        auto tr_read = [&](int j) {  // V^T operand of slot NSS + j: keys 16 t .. 16 t + 15
+            const int t = j / DB, db = j % DB;
+            trv[j][0] = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
+            trv[j][1] = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
+        };
+        // max of key block kb2 in log2 units; keys past the chunk (read as zero) masked
+        auto block_max = [&](int kb2) {
+            if (last) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
-        }
-        // online softmax in base 2 on t = s * scale * log2(e), with a lazily moved max
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+            }
+            float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-        mx = fmaxf(mx, swap_half(mx)) * p.c;
-        if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m = m_new;
-        }
-        u32x4_t pk[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
+            return half_max(mx) * p.c;
+        };
+        auto exps = [&](int t) {  // P^T of keys 16 t .. 16 t + 15 as the B operand
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 8 * (t % 2) + 2 * j;
@@ -291,22 +295,64 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
                 l += p0 + p1;
                 pk[t][j] = pack_bf16x2(p0, p1);
             }
-        // O^T += V^T P^T over the tile's 64 keys (4 k-steps of 16)
+        };
+
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16x8_t pb = as_bf16x8(pk[t]);
+        for (int i = 0; i < PF; ++i) row_read(i);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x2_t v0 = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
-                const u32x2_t v1 = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
-                oacc[db] = mfma32(as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]}), pb, oacc[db]);
+        for (int s = 0; s < NSLOT; ++s) {
+            if (s < NSS) {
+                const int kb2 = s / KS, ks = s % KS;
+                sacc[kb2] = mfma32(stk[s], qreg[ks], ks == 0 ? f32x16_t{} : sacc[kb2]);
+                if (s + PF < NSS) row_read(s + PF);
+            } else {
+                const int j = s - NSS, t = j / DB, db = j % DB;
+                if (j == 2 * DB && late) {
+#pragma unroll
+                    for (int d2 = 0; d2 < DB; ++d2)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[d2][r] *= alpha1;
+                }
+                oacc[db] = mfma32(as_bf16x8(u32x4_t{trv[j][0][0], trv[j][0][1], trv[j][1][0], trv[j][1][1]}),
+                                  as_bf16x8(pk[t]), oacc[db]);
             }
+#pragma unroll
+            for (int j = 0; j < 4 * DB; ++j)
+                if (s == NSS + j - LT) tr_read(j);
+            if (s == KS + 2) {
+                const float mx = block_max(0);
+                if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
+                    const float m_new = fmaxf(m, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+                    l *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    m = m_new;
+                }
+                exps(0);
+            }
+            if (s == KS + 3) exps(1);
+            if (s == NSS + 1) {
+                const float mx = block_max(1);
+                if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
+                    const float m_new = fmaxf(m, mx);
+                    alpha1 = __builtin_amdgcn_exp2f(m - m_new);
+                    l *= alpha1;
+                    m = m_new;
+                    late = true;
+                }
+            }
+            if (s == NSS + 2) exps(2);
+            if (s == NSS + 3) exps(3);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) wait_vmem();
         __syncthreads();
     }
 
-    l += swap_half(l);
+    l = half_sum(l);
     if (!row_ok) return;
     const float inv_l = 1.f / l;
     const float lse_c = m * kLn2 + logf(l);
@@ -637,36 +683,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
     issue(0, 0);
     wait_vmem();
     __syncthreads();
+    // One key tile is a software pipeline of slots holding two MFMAs each: slots [0, NS)
+    // compute S^T and dP^T of key block kb2 = s / KS at k-step s % KS, slots [NS, NSLOT)
+    // add K^T dS^T for 16 keys t and two column blocks.  Row reads run PF slots and
+    // transposing reads LT slots ahead of their MFMAs, the softmax of 16 keys two slots
+    // after its key block's last S/dP MFMA; a scheduling barrier closes every slot.
+    //   Keys past the chunk need no mask: their K rows read as zero, so whatever P and dS
+    // they get, their share of dQ = dS K is zero.
+    constexpr int NS = 2 * KS, SPT = DB / 2, NSLOT = NS + 4 * SPT;
+    constexpr int PF = 3, LT = 2;
+    static_assert(DB % 2 == 0, "two column blocks per slot");
     const int ntiles = (p.Sk + BN - 1) / BN;
     for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1, n0 = it * BN;
+        const int buf = it & 1;
         const bool more = it + 1 < ntiles;
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
-        // S^T = K Q^T and dP^T = V dO^T for two 32-key blocks (lane = query row)
         f32x16_t sacc[2], dpacc[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            sacc[kb2] = f32x16_t{};
-            dpacc[kb2] = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                sacc[kb2] = mfma32(lds_b128((const lds_u16*)(kb + kb2 * 32 * ROWB + ra_off[ks])), qreg[ks], sacc[kb2]);
-                dpacc[kb2] = mfma32(lds_b128((const lds_u16*)(vb + kb2 * 32 * ROWB + ra_off[ks])), oreg[ks], dpacc[kb2]);
-            }
-        }
-        if (n0 + BN > p.Sk) {  // last tile: keys past the chunk read as zero; give them P = 0
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
-        }
-        // dS^T = P^T * (dP^T - delta), packed as the B operand of dQ^T += K^T dS^T
+        bf16x8_t stk[NS], stv[NS];
         u32x4_t dsk[4];
+        u32x2_t trk[4 * SPT][2][2];
+
+        auto row_read = [&](int i) {
+            const int kb2 = i / KS, ks = i % KS;
+            stk[i] = lds_b128((const lds_u16*)(kb + kb2 * 32 * ROWB + ra_off[ks]));
+            stv[i] = lds_b128((const lds_u16*)(vb + kb2 * 32 * ROWB + ra_off[ks]));
+        };
+        auto tr_read = [&](int j) {  // K^T operands of dQ slot j: keys 16 t .. 16 t + 15
+            const int t = j / SPT, db0 = 2 * (j % SPT);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+            for (int u = 0; u < 2; ++u) {
+                trk[j][u][0] = lds_tr((const lds_u16*)(kb + 16 * t * ROWB + tr_off[db0 + u]));
+                trk[j][u][1] = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off8[db0 + u]));
+            }
+        };
+        // dS^T = P^T * (dP^T - delta) of keys 16 t .. 16 t + 15, packed as the B operand
+        auto softmax = [&](int t) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 8 * (t % 2) + 2 * j;
@@ -674,15 +727,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -lse2));
                 dsk[t][j] = pack_bf16x2(p0 * (dpacc[t / 2][r] - dl), p1 * (dpacc[t / 2][r + 1] - dl));
             }
+        };
+
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16x8_t bds = as_bf16x8(dsk[t]);
+        for (int i = 0; i < PF; ++i) row_read(i);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const u32x2_t k0 = lds_tr((const lds_u16*)(kb + 16 * t * ROWB + tr_off[db]));
-                const u32x2_t k1 = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off8[db]));
-                dqacc[db] = mfma32(as_bf16x8(u32x4_t{k0[0], k0[1], k1[0], k1[1]}), bds, dqacc[db]);
+        for (int s = 0; s < NSLOT; ++s) {
+            if (s < NS) {
+                const int kb2 = s / KS, ks = s % KS;
+                sacc[kb2] = mfma32(stk[s], qreg[ks], ks == 0 ? f32x16_t{} : sacc[kb2]);
+                dpacc[kb2] = mfma32(stv[s], oreg[ks], ks == 0 ? f32x16_t{} : dpacc[kb2]);
+                if (s + PF < NS) row_read(s + PF);
+            } else {
+                const int j = s - NS, t = j / SPT, db0 = 2 * (j % SPT);
+                const bf16x8_t bds = as_bf16x8(dsk[t]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    dqacc[db0 + u] = mfma32(
+                        as_bf16x8(u32x4_t{trk[j][u][0][0], trk[j][u][0][1], trk[j][u][1][0], trk[j][u][1][1]}), bds,
+                        dqacc[db0 + u]);
             }
+#pragma unroll
+            for (int j = 0; j < 4 * SPT; ++j)
+                if (s == NS + j - LT) tr_read(j);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (s == (t / 2 + 1) * KS + 1 + t % 2) softmax(t);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (more) wait_vmem();
         __syncthreads();

@@ -39,9 +39,17 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Exchange a value with the lane 32 positions away (lanes l and l^32).
-__device__ __forceinline__ float swap_half(float x) {
-    return __shfl_xor(x, 32, 64);
+// Max and sum of a value over the lane pair (l, l ^ 32).  v_permlane32_swap trades the
+// upper half of its first operand with the lower half of its second; with both operands
+// holding x, every lane ends up with x of both lanes of its pair, in the same order in
+// both halves (so the two lanes get bit-identical sums).
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // The hardware hands consecutive workgroups of a launch to the 8 XCDs in

@@ -392,51 +392,68 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 
 // ============================================================================ backward
 // --------------------------------------------------------------- dK, dV (KV-stationary)
-// Workgroup = 128 keys of the chunk (32 per wavefront) x one query head; sweeps every
-// query row of that head in tiles of 64.  No dQ here (see bwd_dq_bf16_kernel), so the
-// only atomics are the final dK/dV adds shared by the query heads of a GQA group.
+// Workgroup = 128 keys of the chunk x one KV head; sweeps every query row of the query
+// heads sharing that KV head in tiles of 64 (so it owns its dK/dV rows and adds them
+// without atomics).  Each 32-key group has two wavefronts (two per SIMD) with split
+// roles, pipelined one Q tile apart so that each one's softmax arithmetic overlaps the
+// other's MFMAs.  Iteration t (closed by the one barrier of the iteration) runs
+//   role 0: dV += P^T dO of tile t-1, S = Q K^T of tile t, then P = exp2(S c - lse2)
+//           (bf16 packs for its own dV, fp16 copy to LDS for role 1);
+//   role 1: dS = P (dP - delta) of tile t-1 (P from LDS), dP = dO V^T of tile t, and
+//           dK += dS^T Q of tile t-1.
+// Q/dO tiles are triple-buffered (tile t-1 is still read while tile t+1 lands), P
+// double-buffered.  LDS starts zeroed, so the step for "tile -1" adds exact zeros, and
+// one extra iteration drains the last tile (its S/dP run on a finite stale buffer and
+// are discarded).  No dQ here (see bwd_dq_bf16_kernel).
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdParams p) {
     constexpr int KS = D / 16, DB = D / 32, BN = kBwdBlockN, BM = kBwdBlockM;
     constexpr int RB = BM / 32;            // 32-row blocks per Q tile
     constexpr int RC = D / 8;              // 16-byte chunks per row
     constexpr int ROWB = D * 2;            // bytes per (unpadded) tile row
     constexpr int TILEB = BM * ROWB;       // bytes of one Q or dO tile
     constexpr int RPI = 1024 / ROWB;       // rows moved by one wavefront-wide copy
-    constexpr int NI = BM / RPI / 4;       // copies per wavefront per tensor per tile
+    constexpr int NW = 2 * kBwdWaves;      // wavefronts per workgroup
+    constexpr int NI = BM / RPI / NW;      // copies per wavefront per tensor per tile
+    constexpr int NG = 2 * RB;             // 16-row groups per Q tile
     static_assert(RC >= 8 && NI >= 1, "tile geometry");
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [Q0 | dO0 | Q1 | dO1]
-    __shared__ __attribute__((aligned(16))) float stat[2][2][BM];     // [buffer][lse*log2e | delta][row]
+    constexpr int SMEMB = 6 * TILEB;                                  // [Q0 | dO0 | Q1 | dO1 | Q2 | dO2]
+    constexpr int STATB = 3 * 2 * BM * 4;                             // [buffer][lse*log2e | delta][row]
+    constexpr int PBUFB = 2 * kBwdWaves * 2 * RB * 64 * 16;           // [buffer][group][rb, t2][lane] (8 fp16 each)
+    __shared__ __attribute__((aligned(1024))) char smem[SMEMB + STATB + PBUFB];
     RA_LDS char* const lbase = (RA_LDS char*)smem;
+    RA_LDS float* const stat = (RA_LDS float*)(lbase + SMEMB);
+    RA_LDS u32x4_t* const pbuf = (RA_LDS u32x4_t*)(lbase + SMEMB + STATB);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = w % kBwdWaves, role = w / kBwdWaves;
     const int l32 = lane & 31, hh = lane >> 5;
     const int gq = lane >> 4, l16 = lane & 15, e4 = l16 >> 2, a4 = l16 & 3;
     const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
     const int kt = (int)(logical % p.n_tiles);
     const int rest = (int)(logical / p.n_tiles);
-    const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
+    const int Hkv = p.Hq / p.G;
+    const int g = rest % Hkv, b = rest / Hkv;
     const int n0 = kt * BN;
-    const int key = n0 + 32 * w + l32;  // this lane's key (column of S/dP, row of dK/dV)
+    const int key = n0 + 32 * kg + l32;  // this lane's key (column of S/dP, row of dK/dV)
     const bool keys_partial = n0 + BN > p.Sk;
+    const int ntq = (p.Sq + BM - 1) / BM;  // Q tiles per query head
+    const int ntiles = ntq * p.G;          // every Q tile of every query head of the group
 
-    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
-    const uint16_t* vbase = p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
-    const uint16_t* qbase = p.q + (int64_t)b * p.q_sB + (int64_t)h * p.q_sH;
-    const uint16_t* obase = p.dout + (int64_t)b * p.do_sB + (int64_t)h * p.do_sH;
-    const float* lbase_g = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH;
-    const float* dbase_g = p.delta + (int64_t)b * p.d_sB + (int64_t)h * p.d_sH;
+    // zero all of LDS (the "tile -1" step and stale reads see finite values)
+    for (int i = tid; i < (SMEMB + STATB + PBUFB) / 16; i += 64 * NW) ((RA_LDS u32x4_t*)lbase)[i] = u32x4_t{0u, 0u, 0u, 0u};
 
-    bf16x8_t kreg[KS], vreg[KS];
+    // role 0 holds its keys' K rows, role 1 their V rows (the B operand of S or dP)
+    bf16x8_t kvreg[KS];
     {
-        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase, 0, p.k_sS * 2, p.k_bytes);
-        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase, 0, p.v_sS * 2, p.v_bytes);
+        const uint16_t* base = role == 0 ? p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH
+                                         : p.v + (int64_t)b * p.v_sB + (int64_t)g * p.v_sH;
+        const int64_t sS = role == 0 ? p.k_sS : p.v_sS;
+        const uint32_t nbytes = role == 0 ? p.k_bytes : p.v_bytes;
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(base, 0, sS * 2, nbytes);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            kreg[ks] = as_bf16x8(bload16(rk, (uint32_t)((key * p.k_sS + 16 * ks + 8 * hh) * 2), 0));
-            vreg[ks] = as_bf16x8(bload16(rv, (uint32_t)((key * p.v_sS + 16 * ks + 8 * hh) * 2), 0));
-        }
+        for (int ks = 0; ks < KS; ++ks) kvreg[ks] = as_bf16x8(bload16(r, (uint32_t)((key * sS + 16 * ks + 8 * hh) * 2), 0));
     }
     uint32_t vq[NI], vo[NI];
 #pragma unroll
@@ -445,8 +462,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         vo[i] = copy_voff<D>(w * NI + i, lane, p.do_sS);
     }
     float lpre = 0.f, dpre = 0.f;
+    // tile it: Q tile it % ntq of query head g G + it / ntq, into buffer it % 3
     auto issue = [&](int it, int buf) {
-        const int r0 = it * BM;
+        const int hq = g * p.G + it / ntq, r0 = (it % ntq) * BM;
+        const uint16_t* qbase = p.q + (int64_t)b * p.q_sB + (int64_t)hq * p.q_sH;
+        const uint16_t* obase = p.dout + (int64_t)b * p.do_sB + (int64_t)hq * p.do_sH;
         const i32x4_t rq = tile_desc(qbase, r0, p.q_sS * 2, p.q_bytes);
         const i32x4_t ro = tile_desc(obase, r0, p.do_sS * 2, p.do_bytes);
         RA_LDS char* qdst = lbase + (2 * buf) * TILEB;
@@ -458,23 +478,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         }
         if (tid < BM) {
             const uint32_t nbytes = (uint32_t)p.Sq * 4;
-            lpre = bload4f(tile_rsrc(lbase_g, r0, 4, nbytes), (uint32_t)tid * 4, 0);
-            dpre = bload4f(tile_rsrc(dbase_g, r0, 4, nbytes), (uint32_t)tid * 4, 0);
+            const float* lrow = p.lse + (int64_t)b * p.l_sB + (int64_t)hq * p.l_sH;
+            const float* drow = p.delta + (int64_t)b * p.d_sB + (int64_t)hq * p.d_sH;
+            lpre = bload4f(tile_rsrc(lrow, r0, 4, nbytes), (uint32_t)tid * 4, 0);
+            dpre = bload4f(tile_rsrc(drow, r0, 4, nbytes), (uint32_t)tid * 4, 0);
         }
     };
     auto commit_stats = [&](int buf) {
         if (tid < BM) {
-            stat[buf][0][tid] = lpre * kLog2e;
-            stat[buf][1][tid] = dpre;
+            stat[(2 * buf) * BM + tid] = lpre * kLog2e;
+            stat[(2 * buf + 1) * BM + tid] = dpre;
         }
     };
 
-    f32x16_t dkacc[DB], dvacc[DB];
+    // dV (role 0) or dK (role 1) of this group's 32 keys
+    f32x16_t acc[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        dkacc[db] = f32x16_t{};
-        dvacc[db] = f32x16_t{};
-    }
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
     // lane-constant LDS offsets: row reads (S, dP operands) and transposing reads (dV, dK)
     const int sw_row = swz<RC>(l32);
     int ra_off[KS];
@@ -487,118 +507,137 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_bf16_kernel(BwdParams p) {
         tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
         tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
     }
+    const int own_off = role == 0 ? 0 : TILEB;    // S: Q rows, dP: dO rows
+    const int oth_off = role == 0 ? TILEB : 0;    // dV: dO^T, dK: Q^T
 
+    // Iteration slots (two MFMAs each): slot s runs the S/dP MFMA of row block s / KS at
+    // k-step s % KS (tile t) and the dV/dK MFMA of group grp, column block db, j = s
+    // (tile t-1).  Row reads run PF slots, transposing reads LT slots ahead.
+    constexpr int NSLOT = RB * KS, PF = 3, LT = 2;
+    static_assert(NSLOT == NG * DB, "one S/dP and one dV/dK MFMA per slot");
+    u32x4_t pk[RB][2];   // bf16 A-operands of dV (role 0: P) or dK (role 1: dS), tile t-1
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) pk[rb][0] = pk[rb][1] = u32x4_t{0u, 0u, 0u, 0u};
+    f32x16_t sacc[RB];   // S (role 0) or dP (role 1)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x16_t{};
+
+    __syncthreads();  // LDS zeroed
     issue(0, 0);
     wait_vmem();
     commit_stats(0);
+    if (ntiles > 1) issue(1, 1);
     __syncthreads();
-    // One Q tile is a software pipeline of slots holding two MFMAs each: slots [0, NS)
-    // compute S and dP of row block rb = s / KS at k-step s % KS, slots [NS, NSLOT) add
-    // dV and dK of group g = (rb, t2) (16 query rows) and column block db.  Operand
-    // reads are issued PF (row reads) or LT (transposing reads) slots before their
-    // MFMAs; the softmax of a row block runs in the slots after its last S/dP MFMA, its
-    // statistics read one slot earlier.  A scheduling barrier closes every slot, so
-    // the compiler cannot sink a read next to its consumer.
-    //   Keys past the chunk (K = V = 0 there) need no mask: their P and dS only reach
-    // their own rows of the dK/dV accumulators, which are never stored.
-    constexpr int NS = RB * KS, NG = 2 * RB, NSLOT = NS + NG * DB;
-    constexpr int PF = 4, LT = DB < 2 ? DB : 2;
-    static_assert(LT <= DB, "transposing reads must not overwrite operands still in use");
-    const int ntiles = (p.Sq + BM - 1) / BM;
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        const bool more = it + 1 < ntiles;
-        if (more) issue(it + 1, buf ^ 1);
-        const RA_LDS char* qb = lbase + (2 * buf) * TILEB;
-        const RA_LDS char* ob = lbase + (2 * buf + 1) * TILEB;
-        f32x16_t sacc[RB], dpacc[RB];
-        bf16x8_t stq[PF], sto[PF];
-        u32x4_t pp[RB][2], pd[RB][2];       // P and dS as bf16 MFMA A-operands, per (rb, t2)
-        u32x2_t tro[2][DB][2], trq[2][DB][2];
-        f32x4_t sl2[2], sdl[2];
+    int cur = 0;  // buffer of tile t; tile t-1 sits in (cur + 2) % 3
+    for (int it = 0; it <= ntiles; ++it) {
+        const int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
+        const RA_LDS char* rowb = lbase + 2 * cur * TILEB + own_off;
+        const RA_LDS char* trb = lbase + 2 * prv * TILEB + oth_off;
+        RA_LDS u32x4_t* const pw = pbuf + ((it & 1) * kBwdWaves + kg) * (2 * RB) * 64 + lane;        // P of tile t
+        const RA_LDS u32x4_t* const pr = pbuf + (((it + 1) & 1) * kBwdWaves + kg) * (2 * RB) * 64 + lane;  // P of tile t-1
 
-        auto row_read = [&](int i) {
-            const int rb = i / KS, ks = i % KS;
-            stq[i % PF] = lds_b128((const lds_u16*)(qb + 32 * rb * ROWB + ra_off[ks]));
-            sto[i % PF] = lds_b128((const lds_u16*)(ob + 32 * rb * ROWB + ra_off[ks]));
-        };
-        auto tr_read = [&](int grp) {  // dO^T and Q^T operands of query rows 16 grp .. 16 grp + 15
-            const int roff = 16 * grp * ROWB, pb = grp & 1;
+        if (role == 1) {
+            // dS of tile t-1 from its dP (still in sacc), P (fp16 from LDS) and delta
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                tro[pb][db][0] = lds_tr((const lds_u16*)(ob + roff + tr_off[db]));
-                tro[pb][db][1] = lds_tr((const lds_u16*)(ob + roff + 8 * ROWB + tr_off8[db]));
-                trq[pb][db][0] = lds_tr((const lds_u16*)(qb + roff + tr_off[db]));
-                trq[pb][db][1] = lds_tr((const lds_u16*)(qb + roff + 8 * ROWB + tr_off8[db]));
-            }
-        };
-        auto stat_read = [&](int rb, int g4) {
-            const int r = 32 * rb + 8 * g4 + 4 * hh;
-            sl2[g4 & 1] = *(const RA_LDS f32x4_t*)&stat[buf][0][r];
-            sdl[g4 & 1] = *(const RA_LDS f32x4_t*)&stat[buf][1][r];
-        };
-        // lane = key, register 4 g4 + j = query row 32 rb + 8 g4 + 4 hh + j
-        auto softmax = [&](int rb, int g4) {
-            float pv[4], dsv[4];
+            for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -sl2[g4 & 1][j]));
-                dsv[j] = pv[j] * (dpacc[rb][4 * g4 + j] - sdl[g4 & 1][j]);
-            }
-            pp[rb][g4 / 2][2 * (g4 % 2)] = pack_bf16x2(pv[0], pv[1]);
-            pp[rb][g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
-            pd[rb][g4 / 2][2 * (g4 % 2)] = pack_bf16x2(dsv[0], dsv[1]);
-            pd[rb][g4 / 2][2 * (g4 % 2) + 1] = pack_bf16x2(dsv[2], dsv[3]);
-        };
-
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    const u32x4_t ph = pr[(2 * rb + t2) * 64];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) row_read(i);
+                    for (int u = 0; u < 2; ++u) {
+                        const int g4 = 2 * t2 + u;
+                        const f32x4_t dl = *(const RA_LDS f32x4_t*)&stat[(2 * prv + 1) * BM + 32 * rb + 8 * g4 + 4 * hh];
+                        float dsv[4];
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            if (s < NS) {
-                const int rb = s / KS, ks = s % KS;
-                sacc[rb] = mfma32(stq[s % PF], kreg[ks], ks == 0 ? f32x16_t{} : sacc[rb]);
-                dpacc[rb] = mfma32(sto[s % PF], vreg[ks], ks == 0 ? f32x16_t{} : dpacc[rb]);
-                if (s + PF < NS) row_read(s + PF);
-            } else {
-                // dV += P^T dO, dK += dS^T Q over 16 query rows (one MFMA k-step)
-                const int grp = (s - NS) / DB, db = (s - NS) % DB, rb = grp / 2, t2 = grp % 2, pb = grp & 1;
-                dvacc[db] = mfma32(as_bf16x8(pp[rb][t2]),
-                                   as_bf16x8(u32x4_t{tro[pb][db][0][0], tro[pb][db][0][1], tro[pb][db][1][0], tro[pb][db][1][1]}),
-                                   dvacc[db]);
-                dkacc[db] = mfma32(as_bf16x8(pd[rb][t2]),
-                                   as_bf16x8(u32x4_t{trq[pb][db][0][0], trq[pb][db][0][1], trq[pb][db][1][0], trq[pb][db][1][1]}),
-                                   dkacc[db]);
-            }
-#pragma unroll
-            for (int grp = 0; grp < NG; ++grp)
-                if (s == NS + grp * DB - LT) tr_read(grp);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int s0 = (rb + 1) * KS + 1;  // two slots after the row block's last S/dP MFMA
-                if (s >= s0 - 1 && s < s0 + 3) stat_read(rb, s - s0 + 1);
-                if (s >= s0 && s < s0 + 4) softmax(rb, s - s0);
-            }
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t word = ph[2 * u + j / 2];
+                            const float pv = (float)__builtin_bit_cast(_Float16, (uint16_t)(j % 2 ? word >> 16 : word & 0xffffu));
+                            dsv[j] = pv * (sacc[rb][4 * g4 + j] - dl[j]);
+                        }
+                        pk[rb][t2][2 * u] = pack_bf16x2(dsv[0], dsv[1]);
+                        pk[rb][t2][2 * u + 1] = pack_bf16x2(dsv[2], dsv[3]);
+                    }
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
+
+        {
+            bf16x8_t st[NSLOT];
+            u32x2_t tr[NSLOT][2];
+            auto row_read = [&](int s) {
+                st[s] = lds_b128((const lds_u16*)(rowb + 32 * (s / KS) * ROWB + ra_off[s % KS]));
+            };
+            auto tr_read = [&](int j) {  // rows 16 grp .. 16 grp + 15 of tile t-1, columns 32 db ..
+                const int grp = j / DB, db = j % DB, roff = 16 * grp * ROWB;
+                tr[j][0] = lds_tr((const lds_u16*)(trb + roff + tr_off[db]));
+                tr[j][1] = lds_tr((const lds_u16*)(trb + roff + 8 * ROWB + tr_off8[db]));
+            };
+#pragma unroll
+            for (int i = 0; i < PF; ++i) row_read(i);
+#pragma unroll
+            for (int i = 0; i < LT; ++i) tr_read(i);
+#pragma unroll
+            for (int s = 0; s < NSLOT; ++s) {
+                const int rb = s / KS, ks = s % KS, grp = s / DB, db = s % DB;
+                acc[db] = mfma32(as_bf16x8(pk[grp / 2][grp % 2]),
+                                 as_bf16x8(u32x4_t{tr[s][0][0], tr[s][0][1], tr[s][1][0], tr[s][1][1]}), acc[db]);
+                sacc[rb] = mfma32(st[s], kvreg[ks], ks == 0 ? f32x16_t{} : sacc[rb]);
+                if (s + PF < NSLOT) row_read(s + PF);
+                if (s + LT < NSLOT) tr_read(s + LT);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        if (role == 0) {
+            // P of tile t: bf16 packs for the next iteration's dV, fp16 copy for role 1
+            // lane = key, register 4 g4 + j = query row 32 rb + 8 g4 + 4 hh + j
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) {
+                    u32x4_t ph;
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int g4 = 2 * t2 + u;
+                        const f32x4_t l2 = *(const RA_LDS f32x4_t*)&stat[(2 * cur) * BM + 32 * rb + 8 * g4 + 4 * hh];
+                        float pv[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));
+                        pk[rb][t2][2 * u] = pack_bf16x2(pv[0], pv[1]);
+                        pk[rb][t2][2 * u + 1] = pack_bf16x2(pv[2], pv[3]);
+                        ph[2 * u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
+                        ph[2 * u + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
+                    }
+                    pw[(2 * rb + t2) * 64] = ph;
+                }
+        }
+
+        // tile t+1 landed (its copy was issued an iteration ago); tile t-1's buffer and
+        // this iteration's P reads are done by everyone once past the barrier
+        if (it + 1 < ntiles) {
             wait_vmem();
-            commit_stats(buf ^ 1);
+            commit_stats(nxt);
         }
         __syncthreads();
+        if (it + 2 < ntiles) issue(it + 2, prv);
+        cur = nxt;
     }
 
-    // dK, dV rows of this wave's 32 keys: lane = d column, register r = key 8*(r/4) + 4*hh + r%4
-    float* dkb = p.dk + (int64_t)b * p.dk_sB + (int64_t)g * p.dk_sH + (int64_t)(n0 + 32 * w + 4 * hh) * p.dk_sS + l32;
-    float* dvb = p.dv + (int64_t)b * p.dv_sB + (int64_t)g * p.dv_sH + (int64_t)(n0 + 32 * w + 4 * hh) * p.dv_sS + l32;
+    // dV (role 0) or dK (role 1) rows of this group's 32 keys: lane = d column,
+    // register r = key 8*(r/4) + 4*hh + r%4.  The workgroup owns these rows (all query
+    // heads of the group went through it), so a plain read-modify-write adds them.
+    float* const dst = role == 0 ? p.dv + (int64_t)b * p.dv_sB + (int64_t)g * p.dv_sH + (int64_t)(n0 + 32 * kg + 4 * hh) * p.dv_sS + l32
+                                 : p.dk + (int64_t)b * p.dk_sB + (int64_t)g * p.dk_sH + (int64_t)(n0 + 32 * kg + 4 * hh) * p.dk_sS + l32;
+    const int64_t dst_sS = role == 0 ? p.dv_sS : p.dk_sS;
+    const float mul = role == 0 ? 1.f : p.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + (r % 4);
-            if (!keys_partial || n0 + 32 * w + 4 * hh + kr < p.Sk) {
-                unsafeAtomicAdd(dkb + (int64_t)kr * p.dk_sS + 32 * db, p.scale * dkacc[db][r]);
-                unsafeAtomicAdd(dvb + (int64_t)kr * p.dv_sS + 32 * db, dvacc[db][r]);
+            if (!keys_partial || n0 + 32 * kg + 4 * hh + kr < p.Sk) {
+                float* const o = dst + (int64_t)kr * dst_sS + 32 * db;
+                *o += mul * acc[db][r];
             }
         }
 }
@@ -844,11 +883,11 @@ hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra
     p.dv = (float*)dv_acc.data;
     p.dk_sB = dk_acc.sB; p.dk_sS = dk_acc.sS; p.dk_sH = dk_acc.sH;
     p.dv_sB = dv_acc.sB; p.dv_sS = dv_acc.sS; p.dv_sH = dv_acc.sH;
-    // one workgroup per (128-key tile, query head)
+    // one workgroup per (128-key tile, KV head)
     p.n_tiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
-    const unsigned nb = (unsigned)p.n_tiles * q.H * q.B;
-    if (q.D == 64) bwd_kv_bf16_kernel<64><<<nb, 256, 0, s>>>(p);
-    else bwd_kv_bf16_kernel<128><<<nb, 256, 0, s>>>(p);
+    const unsigned nb = (unsigned)p.n_tiles * k.H * q.B;
+    if (q.D == 64) bwd_kv_bf16_kernel<64><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
+    else bwd_kv_bf16_kernel<128><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
     return hipGetLastError();
 }
 

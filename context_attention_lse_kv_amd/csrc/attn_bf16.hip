@@ -17,21 +17,22 @@
 // it surfaces per backend": ring needs LSE for partial-result merging).
 //
 // Backward (one chunk step against that step's own K/V chunk - the point of that
-// issue's "Root cause" and "Expected behavior") runs as two kernels with no dQ
-// atomics.  The KV-stationary kernel owns 128 keys of the chunk (32 per wavefront, K
-// and V in registers) for one query head, sweeps all query rows in LDS tiles of 64,
-// recomputes S = Q K^T and dP = dO V^T with the final LSE and delta, and accumulates
-// dV += P^T dO and dK += dS^T Q in registers (added atomically at the end, because the
-// query heads of a GQA group run in different workgroups).  The Q-stationary kernel
-// owns 128 query rows like the forward, recomputes S^T and dP^T per key tile and
-// accumulates dQ^T += K^T dS^T in registers, so each row's dQ has a single writer.
-// The recompute of S and dP in both kernels (7 products instead of 5) is cheaper on
-// this chip than adding dQ through device-scope atomics from every key tile.
+// issue's "Root cause" and "Expected behavior") runs as two kernels with no atomics.
+// The KV-stationary kernel owns 128 keys of the chunk for one KV head and sweeps the
+// query rows of every query head of that GQA group in LDS tiles of 64; each 32-key
+// group has two wavefronts in split roles (S, P, dV and dP, dS, dK) running one Q
+// tile apart, and the workgroup adds its dK/dV rows with plain read-modify-writes.
+// The Q-stationary kernel owns 128 query rows like the forward, recomputes S^T and
+// dP^T per key tile and accumulates dQ^T += K^T dS^T in registers, so each row's dQ
+// has a single writer.  The recompute of S and dP in both kernels (7 products
+// instead of 5) is cheaper on this chip than adding dQ through device-scope atomics
+// from every key tile.
 //
 // All kernels stream their tiles HBM -> LDS with buffer->LDS copies (rows past the
 // end of a slice arrive as zeros, so tails need no branches), into unpadded rows with
-// an XOR swizzle of 16-byte chunks, double-buffered so that the next tile is in
-// flight while the current one is computed and one barrier per tile suffices.
+// an XOR swizzle of 16-byte chunks, one tile ahead of use, with one barrier per tile;
+// the per-tile work is unrolled into slots closed by scheduling barriers so that the
+// operand reads stay ahead of the MFMAs that consume them.
 #include "ra_device.h"
 
 #define RA_LDS __attribute__((address_space(3)))

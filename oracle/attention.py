@@ -20,6 +20,13 @@ What is computed and where the pages fix it:
   divides the number of query heads.  Reading taken: query head h uses
   key/value head h // (H_q / H_kv) (contiguous groups).
 
+* [P3] (comments on padding tokens to a divisible length): padding changes
+  the result because padded tokens are attended, and a mask is the proposed
+  way out.  Reading taken: an optional key-validity mask ``kmask`` [B, S_k]
+  (nonzero = the key takes part) removes masked keys from every softmax of
+  that batch; a batch with no valid key behaves like an empty key set
+  (lse = -inf, out = 0, zero gradients), and masked keys get dK = dV = 0.
+
 Layouts: q, dout, out are [B, S_q, H_q, D]; k, v are [B, S_k, H_kv, D]
 (batch-first as in [P1] "Reproduction"); lse is [B, H_q, S_q], natural log.
 Inputs are any real arrays; they are upcast to float64.
@@ -50,15 +57,26 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, Hq // Hkv
 
 
-def attention_forward(q, k, v, scale=None, row_block=4096):
-    """Full softmax attention of every query row against every key.
+def _key_sets(kmask, B, Sk):
+    """Indices of the keys each batch attends to (all keys without a mask)."""
+    if kmask is None:
+        return [np.arange(Sk)] * B
+    kmask = np.asarray(kmask)
+    if kmask.shape != (B, Sk):
+        raise ValueError("kmask must be [B, S_k]")
+    return [np.flatnonzero(kmask[b]) for b in range(B)]
+
+
+def attention_forward(q, k, v, scale=None, row_block=4096, kmask=None):
+    """Full softmax attention of every query row against every (valid) key.
 
     For each batch b, query head h (key/value head g = h // G) and query row i:
         s_ij   = scale * <q_i, k_j>
         lse_i  = log(sum_j exp(s_ij))                (natural log)
         out_i  = sum_j exp(s_ij - lse_i) * v_j
-    With no keys (S_k = 0) the softmax is empty: lse = -inf and out = 0, which
-    is the identity element of the LSE merge below.
+    j runs over the keys of batch b that ``kmask`` keeps (all keys without it).
+    With no keys (S_k = 0, or all masked) the softmax is empty: lse = -inf and
+    out = 0, which is the identity element of the LSE merge below.
     Returns (out [B,S_q,H_q,D] float64, lse [B,H_q,S_q] float64).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
@@ -68,12 +86,15 @@ def attention_forward(q, k, v, scale=None, row_block=4096):
         scale = 1.0 / np.sqrt(D)
     out = np.zeros((B, Sq, Hq, D))
     lse = np.full((B, Hq, Sq), -np.inf)
+    keys = _key_sets(kmask, B, Sk)
     if Sk == 0 or Sq == 0:
         return out, lse
     for b in range(B):
+        if keys[b].size == 0:
+            continue
         for h in range(Hq):
             g = h // G
-            kg, vg = k[b, :, g, :], v[b, :, g, :]
+            kg, vg = k[b, keys[b], g, :], v[b, keys[b], g, :]
             for r0 in range(0, Sq, row_block):
                 rows = slice(r0, min(Sq, r0 + row_block))
                 s = scale * (q[b, rows, h, :] @ kg.T)
@@ -85,7 +106,7 @@ def attention_forward(q, k, v, scale=None, row_block=4096):
     return out, lse
 
 
-def attention_backward(q, k, v, dout, scale=None, row_block=4096):
+def attention_backward(q, k, v, dout, scale=None, row_block=4096, kmask=None):
     """Analytic gradients of L = sum(dout * out) for ``attention_forward``.
 
     Softmax-Jacobian form, per (b, h, g = h // G) and rows:
@@ -96,7 +117,9 @@ def attention_backward(q, k, v, dout, scale=None, row_block=4096):
         dQ  = scale * dS K
         dK += scale * dS^T Q
     dK and dV of a key/value head sum the contributions of every query head
-    of its group.  Returns (dq, dk, dv) in float64 with the shapes of q, k, v.
+    of its group; with ``kmask`` the sums run over the valid keys only and
+    masked keys get zero dK and dV.  Returns (dq, dk, dv) in float64 with the
+    shapes of q, k, v.
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     B, Hq, Hkv, G = _check_shapes(q, k, v)
@@ -108,12 +131,16 @@ def attention_backward(q, k, v, dout, scale=None, row_block=4096):
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
+    keys = _key_sets(kmask, B, Sk)
     if Sk == 0 or Sq == 0:
         return dq, dk, dv
     for b in range(B):
+        kb = keys[b]
+        if kb.size == 0:
+            continue
         for h in range(Hq):
             g = h // G
-            kg, vg = k[b, :, g, :], v[b, :, g, :]
+            kg, vg = k[b, kb, g, :], v[b, kb, g, :]
             for r0 in range(0, Sq, row_block):
                 rows = slice(r0, min(Sq, r0 + row_block))
                 qr, dor = q[b, rows, h, :], dout[b, rows, h, :]
@@ -121,12 +148,12 @@ def attention_backward(q, k, v, dout, scale=None, row_block=4096):
                 m = s.max(axis=1)
                 l_row = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
                 p = np.exp(s - l_row[:, None])
-                dv[b, :, g, :] += p.T @ dor
+                dv[b, kb, g, :] += p.T @ dor
                 dp = dor @ vg.T
                 delta = (p * dp).sum(axis=1)
                 ds = p * (dp - delta[:, None])
                 dq[b, rows, h, :] = scale * (ds @ kg)
-                dk[b, :, g, :] += scale * (ds.T @ qr)
+                dk[b, kb, g, :] += scale * (ds.T @ qr)
     return dq, dk, dv
 
 

@@ -18,6 +18,10 @@ Pins used (none of them retypes the oracle's own formula):
                    keys of dV equals the sum of dO over the group's queries;
                    GQA equals MHA with repeated K/V and its dK/dV are the
                    head-group sums
+  key mask       - torch SDPA with a boolean attn_mask (+ autograd); one valid
+                   key; masked keys' values irrelevant and their dK/dV zero;
+                   no valid key gives the empty-softmax result; finite
+                   differences; chunk+merge with per-chunk mask slices
   exchange       - slot rule and gradient 2x of the DeepSpeed PR
                    "_DimZeroAllToAll silently fails to send grads", Testing;
                    shapes of the DeepSpeed issue "DistributedAttention ...
@@ -389,7 +393,134 @@ def pin_ulysses_composition(o):
         assert np.abs(got - direct).max() == golden()["ulysses_exchange_shapes"]["max_abs_diff_same_adapter"]
 
 
+# ----------------------------------------------------------------------------- key mask
+def _mask_case(seed, B, Sq, Sk, Hq, Hkv, D):
+    r = _rng(seed)
+    q = r.standard_normal((B, Sq, Hq, D)); k = r.standard_normal((B, Sk, Hkv, D))
+    v = r.standard_normal((B, Sk, Hkv, D)); d = r.standard_normal((B, Sq, Hq, D))
+    m = (r.random((B, Sk)) < 0.6).astype(np.uint8)
+    m[:, 0] = 1  # every batch keeps at least one key (torch SDPA gives NaN otherwise)
+    return q, k, v, d, m
+
+
+def pin_mask_torch_sdpa(o):
+    for seed, (B, Sq, Sk, Hq, Hkv, D, scale) in enumerate([(3, 9, 21, 4, 2, 8, 0.3), (2, 16, 40, 6, 6, 16, None)]):
+        q, k, v, d, m = _mask_case(30 + seed, B, Sq, Sk, Hq, Hkv, D)
+        sc = scale if scale is not None else 1.0 / math.sqrt(D)
+        G = Hq // Hkv
+        qt = torch.tensor(q).transpose(1, 2).contiguous().requires_grad_(True)
+        kt = torch.tensor(k).transpose(1, 2).contiguous().requires_grad_(True)
+        vt = torch.tensor(v).transpose(1, 2).contiguous().requires_grad_(True)
+        am = torch.tensor(m.astype(bool))[:, None, None, :]  # True = attend
+        out_t = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=sc, enable_gqa=(G > 1))
+        sco = sc * (qt.detach() @ kt.detach().repeat_interleave(G, dim=1).transpose(-1, -2))
+        lse_t = torch.logsumexp(sco.masked_fill(~am, float("-inf")), dim=-1)
+        g_t = torch.autograd.grad(out_t, (qt, kt, vt), torch.tensor(d).transpose(1, 2))
+        out, lse = o.attention_forward(q, k, v, scale=scale, kmask=m)
+        dq, dk, dv = o.attention_backward(q, k, v, d, scale=scale, kmask=m)
+        tr = lambda t: t.detach().transpose(1, 2).numpy()
+        assert _rel(out, tr(out_t)) < 1e-12
+        assert np.abs(lse - lse_t.numpy()).max() < 1e-12
+        for a, b in ((dq, g_t[0]), (dk, g_t[1]), (dv, g_t[2])):
+            assert _rel(a, tr(b)) < 1e-11, _rel(a, tr(b))
+
+
+def pin_mask_single_valid_key(o):
+    r = _rng(33)
+    B, Sq, Sk, Hq, Hkv, D = 2, 6, 7, 4, 2, 5
+    q = r.standard_normal((B, Sq, Hq, D)); k = r.standard_normal((B, Sk, Hkv, D)); v = r.standard_normal((B, Sk, Hkv, D))
+    d = r.standard_normal(q.shape)
+    m = np.zeros((B, Sk), np.uint8); m[0, 3] = 1; m[1, 5] = 1
+    out, lse = o.attention_forward(q, k, v, scale=0.4, kmask=m)
+    dq, dk, dv = o.attention_backward(q, k, v, d, scale=0.4, kmask=m)
+    for b, j in ((0, 3), (1, 5)):
+        for h in range(Hq):
+            g = h // 2
+            assert np.allclose(out[b, :, h, :], np.broadcast_to(v[b, j, g, :], (Sq, D)), rtol=0, atol=1e-14)
+            assert np.allclose(lse[b, h, :], 0.4 * (q[b, :, h, :] @ k[b, j, g, :]), rtol=0, atol=1e-13)
+        for g in range(Hkv):
+            assert np.allclose(dv[b, j, g, :], d[b, :, 2 * g:2 * g + 2, :].sum(axis=(0, 1)), rtol=0, atol=1e-12)
+    assert np.abs(dq).max() < 1e-13 and np.abs(dk).max() < 1e-13
+    keep = np.zeros((B, Sk), bool); keep[0, 3] = keep[1, 5] = True
+    assert np.all(dv[~keep] == 0)
+
+
+def pin_mask_values_irrelevant(o):
+    q, k, v, d, m = _mask_case(34, 2, 8, 15, 4, 2, 8)
+    out, lse = o.attention_forward(q, k, v, kmask=m)
+    grads = o.attention_backward(q, k, v, d, kmask=m)
+    r = _rng(35)
+    k2, v2 = k.copy(), v.copy()
+    k2[m == 0] = 1e3 * r.standard_normal(k2[m == 0].shape); v2[m == 0] = r.standard_normal(v2[m == 0].shape)
+    out2, lse2 = o.attention_forward(q, k2, v2, kmask=m)
+    grads2 = o.attention_backward(q, k2, v2, d, kmask=m)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    for a, b in zip(grads, grads2):
+        assert np.array_equal(a, b)
+    assert np.all(grads[1][m == 0] == 0) and np.all(grads[2][m == 0] == 0)
+    # all-ones mask = no mask
+    ones = np.ones_like(m)
+    a, la = o.attention_forward(q, k, v, kmask=ones)
+    b, lb = o.attention_forward(q, k, v)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def pin_mask_no_valid_key(o):
+    q, k, v, d, m = _mask_case(36, 3, 5, 9, 2, 1, 4)
+    m[1, :] = 0
+    out, lse = o.attention_forward(q, k, v, kmask=m)
+    dq, dk, dv = o.attention_backward(q, k, v, d, kmask=m)
+    assert np.all(np.isneginf(lse[1])) and np.all(out[1] == 0)
+    assert np.all(dq[1] == 0) and np.all(dk[1] == 0) and np.all(dv[1] == 0)
+    assert np.all(np.isfinite(lse[[0, 2]])) and not np.any(np.isnan(out))
+    # the other batches match a run without batch 1
+    sel = [0, 2]
+    o2, l2 = o.attention_forward(q[sel], k[sel], v[sel], kmask=m[sel])
+    assert np.array_equal(o2, out[sel]) and np.array_equal(l2, lse[sel])
+
+
+def pin_mask_finite_differences(o):
+    q, k, v, d, m = _mask_case(37, 1, 4, 6, 2, 1, 3)
+    m[0] = [1, 0, 1, 1, 0, 1]
+    scale = 0.8
+
+    def L(q_, k_, v_):
+        return float((o.attention_forward(q_, k_, v_, scale=scale, kmask=m)[0] * d).sum())
+
+    grads = o.attention_backward(q, k, v, d, scale=scale, kmask=m)
+    h = 1e-6
+    for which, grad in enumerate(grads):
+        args = [q, k, v]
+        base = args[which]
+        fd = np.zeros_like(base)
+        it = np.nditer(base, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = base.copy(); plus[idx] += h
+            minus = base.copy(); minus[idx] -= h
+            ap = list(args); ap[which] = plus
+            am = list(args); am[which] = minus
+            fd[idx] = (L(*ap) - L(*am)) / (2 * h)
+        assert _rel(grad, fd) < 1e-6, (which, _rel(grad, fd))
+
+
+def pin_mask_chunk_merge(o):
+    q, k, v, d, m = _mask_case(38, 2, 7, 20, 2, 2, 4)
+    m[0, 8:15] = 0  # the second chunk is fully masked for batch 0
+    full_out, full_lse = o.attention_forward(q, k, v, scale=0.5, kmask=m)
+    lens, order = [8, 7, 5], [1, 2, 0]
+    starts = [0, 8, 15]
+    acc_out = np.zeros(q.shape); acc_lse = np.full((q.shape[0], q.shape[2], q.shape[1]), -np.inf)
+    for j in order:
+        sl = slice(starts[j], starts[j] + lens[j])
+        po, pl = o.attention_forward(q, k[:, sl], v[:, sl], scale=0.5, kmask=m[:, sl])
+        acc_out, acc_lse = o.merge_lse(acc_out, acc_lse, po, pl)
+    assert np.abs(acc_out - full_out).max() < 1e-12 and np.abs(acc_lse - full_lse).max() < 1e-12
+
+
 ALL_PINS = [
+    pin_mask_torch_sdpa, pin_mask_single_valid_key, pin_mask_values_irrelevant, pin_mask_no_valid_key,
+    pin_mask_finite_differences, pin_mask_chunk_merge,
     pin_single_key, pin_zero_query, pin_equal_keys, pin_no_keys, pin_default_scale,
     pin_torch_sdpa, pin_finite_differences, pin_chunk_merge_invariance, pin_merge_closed_forms,
     pin_gradient_invariants, pin_gqa_group_sums, pin_rejects_bad_gqa, pin_delta_identity,

@@ -16,9 +16,13 @@ MUTANTS = [
     ("attention.py", "ds = p * (dp - delta[:, None])", "ds = p * dp"),
     ("attention.py", "(dp - delta[:, None])", "(dp + delta[:, None])"),
     ("attention.py", "dq[b, rows, h, :] = scale * (ds @ kg)", "dq[b, rows, h, :] = (ds @ kg)"),
-    ("attention.py", "dk[b, :, g, :] += scale * (ds.T @ qr)", "dk[b, :, g, :] += scale * (ds.T @ dor)"),
-    ("attention.py", "dv[b, :, g, :] += p.T @ dor", "dv[b, :, g, :] += p.T @ qr"),
-    ("attention.py", "dv[b, :, g, :] += p.T @ dor", "dv[b, :, g, :] = p.T @ dor"),
+    ("attention.py", "dk[b, kb, g, :] += scale * (ds.T @ qr)", "dk[b, kb, g, :] += scale * (ds.T @ dor)"),
+    ("attention.py", "dv[b, kb, g, :] += p.T @ dor", "dv[b, kb, g, :] += p.T @ qr"),
+    ("attention.py", "dv[b, kb, g, :] += p.T @ dor", "dv[b, kb, g, :] = p.T @ dor"),
+    ("attention.py", "return [np.flatnonzero(kmask[b]) for b in range(B)]", "return [np.flatnonzero(kmask[0]) for b in range(B)]"),
+    ("attention.py", "kg, vg = k[b, keys[b], g, :], v[b, keys[b], g, :]", "kg, vg = k[b, keys[b], g, :], v[b, :keys[b].size, g, :]"),
+    ("attention.py", "dv[b, kb, g, :] += p.T @ dor", "dv[b, :kb.size, g, :] += p.T @ dor"),
+    ("attention.py", "kg, vg = k[b, kb, g, :], v[b, kb, g, :]", "kg, vg = k[b, :, g, :][kb], v[b, :, g, :][kb[::-1]]"),
     ("attention.py", "delta = (p * dp).sum(axis=1)", "delta = (p * dp).sum(axis=0).mean()"),
     ("attention.py", "g = h // G", "g = h % Hkv"),
     ("attention.py", "l_row = m + np.log(", "l_row = m + np.log2("),

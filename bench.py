@@ -73,9 +73,13 @@ def setup(Sq_rows, full):
     return w, lens, order, gq, gk, gv, gdo
 
 
-def run_workload(full, steps, warmup):
+MASK_RECIPE = dict(p_keep=0.95, valid_len=(30000,))  # right padding past 30000 keys + 5 % random holes
+
+
+def run_workload(full, steps, warmup, masked=False):
     w, lens, order, q, k, v, do = setup(4096, full)
     ch = ra.Chunks(lens, order)
+    km = W.make_key_mask(w.B, w.S, 990, **MASK_RECIPE).to(q.device) if masked else None
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((w.B, w.Hq, q.shape[1]), dtype=torch.float32, device=q.device)
     dq, dk, dv = (torch.empty(t.shape, dtype=torch.bfloat16, device=q.device) for t in (q, k, v))
@@ -85,10 +89,10 @@ def run_workload(full, steps, warmup):
                       device=q.device)
 
     def fwd():
-        ra.ring_fwd(q, k, v, ch, out=out, lse=lse, workspace=fws)
+        ra.ring_fwd(q, k, v, ch, out=out, lse=lse, workspace=fws, kmask=km)
 
     def bwd():
-        ra.ring_bwd(q, k, v, out, do, lse, ch, workspace=bws, dq=dq, dk=dk, dv=dv)
+        ra.ring_bwd(q, k, v, out, do, lse, ch, workspace=bws, dq=dq, dk=dk, dv=dv, kmask=km)
 
     def step():
         fwd()
@@ -99,7 +103,7 @@ def run_workload(full, steps, warmup):
     t_bwd = timed(bwd, max(3, steps // 2), 1)
     f_f, f_b = flops(w.B, w.Hq, q.shape[1], w.S, w.D)
     return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, t_step=t_step, t_fwd=t_fwd,
-                t_bwd=t_bwd, f_f=f_f, f_b=f_b)
+                t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km)
 
 
 def dominant_kernel(r, launches=8):
@@ -183,6 +187,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip the full-Q sweep (extra field)")
+    ap.add_argument("--no-masked", action="store_true", help="skip the key-masked sweep (extra field)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only launch the dominant kernel (for hardware-counter runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -253,6 +258,17 @@ def main():
                          "fwd_tflops": round(rf["f_f"] / rf["t_fwd"] / 1e12, 2),
                          "bwd_tflops": round(rf["f_b"] / rf["t_bwd"] / 1e12, 2)}
         del rf
+        torch.cuda.empty_cache()
+    if not args.no_masked:
+        rm = run_workload(False, max(3, args.steps // 2), 1, masked=True)
+        tm = rm["f_f"] + rm["f_b"]
+        res["masked"] = {"mask": "keys >= 30000 of 32768 masked (right padding) + 5 % random holes, seed 990",
+                         "valid_key_fraction": round(float(rm["km"].float().mean()), 4),
+                         "ms_per_step": round(rm["t_step"] * 1e3, 3),
+                         "tflops_dense_count": round(tm / rm["t_step"] / 1e12, 2),
+                         "fwd_tflops": round(rm["f_f"] / rm["t_fwd"] / 1e12, 2),
+                         "bwd_tflops": round(rm["f_b"] / rm["t_bwd"] / 1e12, 2)}
+        del rm
         torch.cuda.empty_cache()
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     print(json.dumps(res), flush=True)

@@ -19,6 +19,8 @@ STATUS_NAMES = ["RA_OK", "RA_E_ARG", "RA_E_SHAPE", "RA_E_DTYPE", "RA_E_ALIGN", "
 EXPORTS = [
     "ra_fwd_chunk", "ra_merge_lse", "ra_bwd_delta", "ra_bwd_chunk", "ra_bwd_chunk_dkdv", "ra_bwd_chunk_dq",
     "ra_ring_fwd", "ra_ring_bwd",
+    "ra_fwd_chunk_masked", "ra_bwd_chunk_masked", "ra_bwd_chunk_dkdv_masked", "ra_bwd_chunk_dq_masked",
+    "ra_ring_fwd_masked", "ra_ring_bwd_masked",
     "ra_ring_fwd_workspace_bytes", "ra_ring_bwd_workspace_bytes", "ra_seq_head_permute",
     "ra_split_sizes", "ra_ring_order", "ra_status_string", "ra_last_error", "ra_version",
 ]
@@ -35,6 +37,10 @@ class RaLse(ctypes.Structure):
                 ("sB", ctypes.c_int64), ("sH", ctypes.c_int64)]
 
 
+class RaKMask(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("sB", ctypes.c_int64)]
+
+
 class RaChunks(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("start", ctypes.POINTER(ctypes.c_int32)),
                 ("len", ctypes.POINTER(ctypes.c_int32)), ("order", ctypes.POINTER(ctypes.c_int32))]
@@ -43,6 +49,7 @@ class RaChunks(ctypes.Structure):
 T = ctypes.POINTER(RaTensor)
 L = ctypes.POINTER(RaLse)
 C = ctypes.POINTER(RaChunks)
+K = ctypes.POINTER(RaKMask)
 vp, f32, i32, sz = ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_size_t
 I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -55,6 +62,12 @@ _SIGS = {
     "ra_bwd_chunk_dq": (i32, [T, T, T, T, L, L, f32, T, vp]),
     "ra_ring_fwd": (i32, [T, T, T, C, f32, T, L, vp, sz, vp]),
     "ra_ring_bwd": (i32, [T, T, T, T, T, L, C, f32, T, T, T, vp, sz, vp]),
+    "ra_fwd_chunk_masked": (i32, [T, T, T, K, f32, T, L, i32, vp]),
+    "ra_bwd_chunk_masked": (i32, [T, T, T, T, L, L, K, f32, T, T, T, i32, vp]),
+    "ra_bwd_chunk_dkdv_masked": (i32, [T, T, T, T, L, L, K, f32, T, T, i32, vp]),
+    "ra_bwd_chunk_dq_masked": (i32, [T, T, T, T, L, L, K, f32, T, vp]),
+    "ra_ring_fwd_masked": (i32, [T, T, T, K, C, f32, T, L, vp, sz, vp]),
+    "ra_ring_bwd_masked": (i32, [T, T, T, T, T, L, K, C, f32, T, T, T, vp, sz, vp]),
     "ra_ring_fwd_workspace_bytes": (sz, [T, T]),
     "ra_ring_bwd_workspace_bytes": (sz, [T, T, T, T, T]),
     "ra_seq_head_permute": (i32, [T, i32, T, i32, i32, vp]),

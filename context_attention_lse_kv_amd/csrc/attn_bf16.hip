@@ -55,6 +55,8 @@ struct FwdParams {
     int B, Sq, Sk, Hq, G, n_qtiles;
     uint32_t k_bytes, v_bytes;  // bytes spanned by one (batch, kv head) slice of the chunk
     float c;                    // scale * log2(e)
+    const uint8_t* km;          // key mask of the chunk (km[b * km_sB + key] != 0: key takes part), or null
+    int64_t km_sB;
 };
 
 struct BwdParams {
@@ -73,6 +75,8 @@ struct BwdParams {
     int B, Sq, Sk, Hq, G, n_tiles;  // tiles along the kernel's stationary axis (keys or query rows)
     uint32_t q_bytes, do_bytes, k_bytes, v_bytes;
     float scale, c;
+    const uint8_t* km;  // key mask of the chunk (km[b * km_sB + key] != 0: key takes part), or null
+    int64_t km_sB;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -99,6 +103,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 
 __device__ __forceinline__ bf16x8_t lds_b128(const lds_u16* p) {
     return __builtin_bit_cast(bf16x8_t, *(const RA_LDS u32x4_t*)p);
+}
+
+// Key-mask bits: lane l of a wavefront loads the mask byte of key n0 + l of a 64-key
+// tile (bytes past the chunk read as 0, i.e. masked); a ballot turns them into one
+// 64-bit word per tile.  In a 32x32 accumulator whose rows or columns are keys, register
+// r of lane l holds key 8 (r / 4) + 4 (l / 32) + r % 4 of its 32-key block kb2.
+__device__ __forceinline__ uint32_t load_key_byte(const uint8_t* km_b, int Sk, int n0, int lane) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(km_b, (uint32_t)Sk);
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (uint32_t)(n0 + lane), 0, 0);
+}
+__device__ __forceinline__ bool key_bit(uint64_t lane_bits, int kb2, int r) {
+    return (lane_bits >> (32 * kb2 + 8 * (r / 4) + (r % 4))) & 1u;
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane
@@ -170,7 +186,7 @@ __device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
 }
 
 // ============================================================================ forward
-template <int D, bool MERGE>
+template <int D, bool MERGE, bool MASK>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
     constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
@@ -212,6 +228,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         vk[i] = copy_voff<D>(w * NI + i, lane, p.k_sS);
         vv[i] = copy_voff<D>(w * NI + i, lane, p.v_sS);
     }
+    const uint8_t* km_b = MASK ? p.km + (int64_t)b * p.km_sB : nullptr;
+    uint32_t kbyte = 0;  // mask byte of key n0 + lane of the tile in flight
     auto issue = [&](int it, int buf) {
         const int r0 = it * BN;
         const i32x4_t rk = tile_desc(kbase, r0, p.k_sS * 2, p.k_bytes);
@@ -223,6 +241,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
             dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
             dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
         }
+        if (MASK) kbyte = load_key_byte(km_b, p.Sk, r0, lane);
     };
     // lane-constant LDS offsets: K row reads (S^T operand) and transposing V reads (V^T operand)
     const int sw_row = swz<RC>(l32);
@@ -250,6 +269,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     //   The running max moves lazily (only when a block exceeds it by more than
     // kRescale, in log2 units).  A move triggered by block 1 rescales l at once but the
     // O accumulator only after the P V MFMAs of block 0, which still use the old max.
+    //   With a key mask, masked keys get s = -inf; a row that has seen no valid key yet
+    // keeps m = -inf and takes its exponentials against 0 (all its scores are -inf).
     constexpr int NSS = 2 * KS, NSLOT = NSS + 4 * DB;
     constexpr int PF = 4, LT = 2;
     const int ntiles = (p.Sk + BN - 1) / BN;
@@ -257,6 +278,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         const int buf = it & 1, n0 = it * BN;
         const bool more = it + 1 < ntiles;
         const bool last = n0 + BN > p.Sk;
+        const uint64_t kl = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) >> (4 * hh) : 0;  // this tile's key bits
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
@@ -275,9 +297,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
             trv[j][0] = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
             trv[j][1] = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
         };
-        // max of key block kb2 in log2 units; keys past the chunk (read as zero) masked
+        // max of key block kb2 in log2 units; keys past the chunk (read as zero) and
+        // masked keys get -inf
         auto block_max = [&](int kb2) {
-            if (last) {
+            if (MASK) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (!key_bit(kl, kb2, r)) sacc[kb2][r] = -INFINITY;
+            } else if (last) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
@@ -288,11 +315,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
             return half_max(mx) * p.c;
         };
         auto exps = [&](int t) {  // P^T of keys 16 t .. 16 t + 15 as the B operand
+            const float ms = MASK && m == -INFINITY ? 0.f : m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 8 * (t % 2) + 2 * j;
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -m));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -m));
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -ms));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -ms));
                 l += p0 + p1;
                 pk[t][j] = pack_bf16x2(p0, p1);
             }
@@ -355,10 +383,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 
     l = half_sum(l);
     if (!row_ok) return;
-    const float inv_l = 1.f / l;
-    const float lse_c = m * kLn2 + logf(l);
     float* orow = p.out + (int64_t)b * p.o_sB + (int64_t)row * p.o_sS + (int64_t)h * p.o_sH;
     float* lp = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row;
+    if (MASK && l == 0.f) {
+        // every key of the chunk masked: the step's partial is the merge identity
+        if (!MERGE) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (hh == 0) *lp = -INFINITY;
+        }
+        return;
+    }
+    const float inv_l = 1.f / l;
+    const float lse_c = m * kLn2 + logf(l);
     if (!MERGE) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -631,12 +670,19 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                                  : p.dk + (int64_t)b * p.dk_sB + (int64_t)g * p.dk_sH + (int64_t)(n0 + 32 * kg + 4 * hh) * p.dk_sS + l32;
     const int64_t dst_sS = role == 0 ? p.dv_sS : p.dk_sS;
     const float mul = role == 0 ? 1.f : p.scale;
+    // a masked key gets no dK/dV at all: its P and dS only ever reached its own
+    // accumulator rows (lane = key in S/dP), so those rows are simply not added
+    uint64_t kl_own = ~0ull;
+    if (p.km) {
+        const uint32_t kbyte = load_key_byte(p.km + (int64_t)b * p.km_sB, p.Sk, n0 + 32 * kg, lane & 31);
+        kl_own = __builtin_amdgcn_ballot_w64(kbyte != 0 && lane < 32) >> (4 * hh);
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + (r % 4);
-            if (!keys_partial || n0 + 32 * kg + 4 * hh + kr < p.Sk) {
+            if ((!keys_partial || n0 + 32 * kg + 4 * hh + kr < p.Sk) && key_bit(kl_own, 0, r)) {
                 float* const o = dst + (int64_t)kr * dst_sS + 32 * db;
                 *o += mul * acc[db][r];
             }
@@ -649,7 +695,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
 // S^T = K Q^T and dP^T = V dO^T (lane = query row), P^T and dS^T with the final LSE and
 // delta, then dQ^T += K^T dS^T with K^T read transposed from the K tile.  Each row's
 // dQ is owned by one lane pair, so the fp32 accumulator is updated without atomics.
-template <int D>
+template <int D, bool MASK>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
     constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
     constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
@@ -692,6 +738,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
         vk[i] = copy_voff<D>(w * NI + i, lane, p.k_sS);
         vv[i] = copy_voff<D>(w * NI + i, lane, p.v_sS);
     }
+    const uint8_t* km_b = MASK ? p.km + (int64_t)b * p.km_sB : nullptr;
+    uint32_t kbyte = 0;  // mask byte of key n0 + lane of the tile in flight
     auto issue = [&](int it, int buf) {
         const int r0 = it * BN;
         const i32x4_t rk = tile_desc(kbase, r0, p.k_sS * 2, p.k_bytes);
@@ -703,6 +751,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
             dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
             dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
         }
+        if (MASK) kbyte = load_key_byte(km_b, p.Sk, r0, lane);
     };
     const int sw_row = swz<RC>(l32);
     int ra_off[KS];
@@ -729,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
     // transposing reads LT slots ahead of their MFMAs, the softmax of 16 keys two slots
     // after its key block's last S/dP MFMA; a scheduling barrier closes every slot.
     //   Keys past the chunk need no mask: their K rows read as zero, so whatever P and dS
-    // they get, their share of dQ = dS K is zero.
+    // they get, their share of dQ = dS K is zero.  Masked keys (key mask) get dS = 0.
     constexpr int NS = 2 * KS, SPT = DB / 2, NSLOT = NS + 4 * SPT;
     constexpr int PF = 3, LT = 2;
     static_assert(DB % 2 == 0, "two column blocks per slot");
@@ -737,6 +786,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
         const bool more = it + 1 < ntiles;
+        const uint64_t kl = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) >> (4 * hh) : 0;  // this tile's key bits
         if (more) issue(it + 1, buf ^ 1);
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
@@ -765,7 +815,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
                 const int r = 8 * (t % 2) + 2 * j;
                 const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -lse2));
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -lse2));
-                dsk[t][j] = pack_bf16x2(p0 * (dpacc[t / 2][r] - dl), p1 * (dpacc[t / 2][r + 1] - dl));
+                float d0 = p0 * (dpacc[t / 2][r] - dl), d1 = p1 * (dpacc[t / 2][r + 1] - dl);
+                if (MASK) {
+                    d0 = key_bit(kl, t / 2, r) ? d0 : 0.f;
+                    d1 = key_bit(kl, t / 2, r + 1) ? d1 : 0.f;
+                }
+                dsk[t][j] = pack_bf16x2(d0, d1);
             }
         };
 
@@ -815,8 +870,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
 
 }  // namespace
 
-hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
-                                 const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
+                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     FwdParams p;
     p.q = (const uint16_t*)q.data;
@@ -835,12 +890,15 @@ hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     p.v_bytes = span_bytes(v.S, v.sS, v.D);
     p.c = scale * 1.4426950408889634f;
     const unsigned nb = (unsigned)p.n_qtiles * q.H * q.B;
+    p.km = km.data;
+    p.km_sB = km.sB;
+    const bool mk = km.data != nullptr;
     if (q.D == 64) {
-        if (merge) fwd_bf16_kernel<64, true><<<nb, 256, 0, s>>>(p);
-        else fwd_bf16_kernel<64, false><<<nb, 256, 0, s>>>(p);
+        if (merge) mk ? fwd_bf16_kernel<64, true, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<64, true, false><<<nb, 256, 0, s>>>(p);
+        else mk ? fwd_bf16_kernel<64, false, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<64, false, false><<<nb, 256, 0, s>>>(p);
     } else {
-        if (merge) fwd_bf16_kernel<128, true><<<nb, 256, 0, s>>>(p);
-        else fwd_bf16_kernel<128, false><<<nb, 256, 0, s>>>(p);
+        if (merge) mk ? fwd_bf16_kernel<128, true, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<128, true, false><<<nb, 256, 0, s>>>(p);
+        else mk ? fwd_bf16_kernel<128, false, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<128, false, false><<<nb, 256, 0, s>>>(p);
     }
     return hipGetLastError();
 }
@@ -876,14 +934,16 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
 }  // namespace
 
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                                const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
-                                const ra_tensor& dv_acc, hipStream_t s) {
+                                const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
     p.dk = (float*)dk_acc.data;
     p.dv = (float*)dv_acc.data;
     p.dk_sB = dk_acc.sB; p.dk_sS = dk_acc.sS; p.dk_sH = dk_acc.sH;
     p.dv_sB = dv_acc.sB; p.dv_sS = dv_acc.sS; p.dv_sH = dv_acc.sH;
+    p.km = km.data;
+    p.km_sB = km.sB;
     // one workgroup per (128-key tile, KV head)
     p.n_tiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
     const unsigned nb = (unsigned)p.n_tiles * k.H * q.B;
@@ -893,8 +953,8 @@ hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra
 }
 
 hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                              const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                              hipStream_t s) {
+                              const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                              const ra_tensor& dq_acc, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
     p.dq = (float*)dq_acc.data;
@@ -902,8 +962,15 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
     // one workgroup per (128-row query tile, query head)
     p.n_tiles = (q.S + kFwdBlockM - 1) / kFwdBlockM;
     const unsigned nb = (unsigned)p.n_tiles * q.H * q.B;
-    if (q.D == 64) bwd_dq_bf16_kernel<64><<<nb, 256, 0, s>>>(p);
-    else bwd_dq_bf16_kernel<128><<<nb, 256, 0, s>>>(p);
+    p.km = km.data;
+    p.km_sB = km.sB;
+    if (km.data) {
+        if (q.D == 64) bwd_dq_bf16_kernel<64, true><<<nb, 256, 0, s>>>(p);
+        else bwd_dq_bf16_kernel<128, true><<<nb, 256, 0, s>>>(p);
+    } else {
+        if (q.D == 64) bwd_dq_bf16_kernel<64, false><<<nb, 256, 0, s>>>(p);
+        else bwd_dq_bf16_kernel<128, false><<<nb, 256, 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

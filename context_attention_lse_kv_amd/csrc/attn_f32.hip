@@ -2,7 +2,9 @@
 // of the ring path, for inputs that are fp32 end to end.  These are VALU kernels:
 // a query row (forward, dQ) or a key row (dK/dV) is owned by T = D/32 lanes, each
 // holding 32 of its D elements; dot products are reduced across those lanes.
-// K/V (or Q/dO) tiles are staged in LDS and read by broadcast.
+// K/V (or Q/dO) tiles are staged in LDS and read by broadcast.  With a key mask,
+// masked keys are skipped (forward, dQ) or get no dK/dV (dK/dV kernel); a forward row
+// that meets no valid key in the chunk yields the merge identity (out 0, lse -inf).
 #include "ra_device.h"
 
 namespace ra {
@@ -11,6 +13,10 @@ namespace {
 constexpr int kThreads = 128;
 constexpr int kTile = 32;  // rows per LDS tile
 constexpr int kSub = 32;   // elements of a row held by one lane
+
+__device__ __forceinline__ bool key_on(const KeyMask& km, int b, int key) {
+    return km.data == nullptr || km.data[(int64_t)b * km.sB + key] != 0;
+}
 
 __device__ __forceinline__ const float* rowp(const ra_tensor& t, int b, int s, int h) {
     return (const float*)t.data + (int64_t)b * t.sB + (int64_t)s * t.sS + (int64_t)h * t.sH;
@@ -35,8 +41,8 @@ __device__ __forceinline__ void stage_rows(float (*lds)[D], const ra_tensor& t, 
 
 // ---------------------------------------------------------------- forward chunk step
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(ra_tensor q, ra_tensor k, ra_tensor v, float scale,
-                                                           ra_tensor out, ra_lse lse, int merge) {
+__global__ __launch_bounds__(kThreads) void fwd_f32_kernel(ra_tensor q, ra_tensor k, ra_tensor v, KeyMask km,
+                                                           float scale, ra_tensor out, ra_lse lse, int merge) {
     constexpr int T = D / kSub;
     constexpr int RowsPerBlock = kThreads / T;
     __shared__ float Ks[kTile][D];
@@ -59,6 +65,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(ra_tensor q, ra_tenso
         __syncthreads();
         const int nk = min(kTile, k.S - n0);
         for (int j = 0; j < nk; ++j) {
+            if (!key_on(km, b, n0 + j)) continue;
             float s = 0.f;
             for (int e = 0; e < kSub; ++e) s += qr[e] * Ks[j][part * kSub + e];
             s = group_sum<T>(s) * scale;
@@ -76,6 +83,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(ra_tensor q, ra_tenso
     if (!valid) return;
     float* orow = (float*)out.data + (int64_t)b * out.sB + (int64_t)row * out.sS + (int64_t)h * out.sH + part * kSub;
     float* lrow = lse.data + (int64_t)b * lse.sB + (int64_t)h * lse.sH + row;
+    if (l == 0.f) {  // no valid key in the chunk: the partial is the merge identity
+        if (!merge) {
+            for (int e = 0; e < kSub; ++e) orow[e] = 0.f;
+            if (part == 0) *lrow = -INFINITY;
+        }
+        return;
+    }
     const float lse_c = m + logf(l);
     const float inv_l = 1.f / l;
     if (!merge) {
@@ -96,7 +110,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(ra_tensor q, ra_tenso
 // ---------------------------------------------------------------- backward: dQ of a chunk
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(ra_tensor q, ra_tensor k, ra_tensor v, ra_tensor dout,
-                                                              ra_lse lse, ra_lse delta, float scale, ra_tensor dq) {
+                                                              ra_lse lse, ra_lse delta, KeyMask km, float scale,
+                                                              ra_tensor dq) {
     constexpr int T = D / kSub;
     constexpr int RowsPerBlock = kThreads / T;
     __shared__ float Ks[kTile][D];
@@ -121,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(ra_tensor q, ra_te
         __syncthreads();
         const int nk = min(kTile, k.S - n0);
         for (int j = 0; j < nk; ++j) {
+            if (!key_on(km, b, n0 + j)) continue;
             float s = 0.f, dp = 0.f;
             for (int e = 0; e < kSub; ++e) {
                 s += qr[e] * Ks[j][part * kSub + e];
@@ -143,8 +159,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(ra_tensor q, ra_te
 // head of the key's group, staged through LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(ra_tensor q, ra_tensor k, ra_tensor v, ra_tensor dout,
-                                                                ra_lse lse, ra_lse delta, float scale, ra_tensor dk,
-                                                                ra_tensor dv) {
+                                                                ra_lse lse, ra_lse delta, KeyMask km, float scale,
+                                                                ra_tensor dk, ra_tensor dv) {
     constexpr int T = D / kSub;
     constexpr int RowsPerBlock = kThreads / T;
     __shared__ float Qs[kTile][D];
@@ -192,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(ra_tensor q, ra_
             }
         }
     }
-    if (!valid) return;
+    if (!valid || !key_on(km, b, key)) return;  // a masked key gets no dK/dV
     float* kd = (float*)dk.data + (int64_t)b * dk.sB + (int64_t)key * dk.sS + (int64_t)g * dk.sH + part * kSub;
     float* vd = (float*)dv.data + (int64_t)b * dv.sB + (int64_t)key * dv.sS + (int64_t)g * dv.sH + part * kSub;
     for (int e = 0; e < kSub; ++e) {
@@ -203,37 +219,37 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(ra_tensor q, ra_
 
 }  // namespace
 
-hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
-                                const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
+                                float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
     if (q.S == 0) return hipSuccess;
     const int T = q.D / kSub;
     dim3 grid((q.S + kThreads / T - 1) / (kThreads / T), q.H, q.B);
     if (q.D == 64)
-        fwd_f32_kernel<64><<<grid, kThreads, 0, s>>>(q, k, v, scale, out, lse, merge);
+        fwd_f32_kernel<64><<<grid, kThreads, 0, s>>>(q, k, v, km, scale, out, lse, merge);
     else
-        fwd_f32_kernel<128><<<grid, kThreads, 0, s>>>(q, k, v, scale, out, lse, merge);
+        fwd_f32_kernel<128><<<grid, kThreads, 0, s>>>(q, k, v, km, scale, out, lse, merge);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                             const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                             hipStream_t s) {
+                             const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                             const ra_tensor& dq_acc, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     const int rpb = kThreads / (q.D / kSub);
     dim3 g((q.S + rpb - 1) / rpb, q.H, q.B);
-    if (q.D == 64) bwd_dq_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
-    else bwd_dq_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dq_acc);
+    if (q.D == 64) bwd_dq_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, km, scale, dq_acc);
+    else bwd_dq_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, km, scale, dq_acc);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dkdv_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                               const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
-                               const ra_tensor& dv_acc, hipStream_t s) {
+                               const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                               const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     const int rpb = kThreads / (q.D / kSub);
     dim3 g((k.S + rpb - 1) / rpb, k.H, k.B);
-    if (q.D == 64) bwd_dkdv_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
-    else bwd_dkdv_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, scale, dk_acc, dv_acc);
+    if (q.D == 64) bwd_dkdv_f32_kernel<64><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, km, scale, dk_acc, dv_acc);
+    else bwd_dkdv_f32_kernel<128><<<g, kThreads, 0, s>>>(q, k, v, dout, lse, delta, km, scale, dk_acc, dv_acc);
     return hipGetLastError();
 }
 

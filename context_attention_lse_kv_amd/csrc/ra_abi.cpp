@@ -216,8 +216,27 @@ ra_lse contiguous_rows(void* data, int32_t B, int32_t H, int32_t S) {
     return r;
 }
 
-ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
-                            const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+// Validation of an optional key mask over S keys of B batches (NULL = no mask).
+ra_status check_kmask(const ra_kmask* m, int32_t B, int32_t S) {
+    if (!m) return RA_OK;
+    if (m->B != B || m->S != S)
+        return fail(RA_E_SHAPE, "kmask: shape [%d,%d] does not match [B,S_k]=[%d,%d]", m->B, m->S, B, S);
+    if (m->sB < 0) return fail(RA_E_ARG, "kmask: negative stride");
+    if (B > 1 && m->sB < S) return fail(RA_E_ARG, "kmask: sB < S makes rows overlap");
+    if ((int64_t)B * S > 0 && !m->data) return fail(RA_E_ARG, "kmask: data is NULL");
+    return RA_OK;
+}
+
+// The kernels' view of the mask rows [start, start + len) of every batch.
+ra::KeyMask key_mask(const ra_kmask* m, int32_t start = 0) {
+    ra::KeyMask r;
+    r.data = m ? m->data + start : nullptr;
+    r.sB = m ? m->sB : 0;
+    return r;
+}
+
+ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra::KeyMask& km,
+                            float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
     if (k.S == 0) {
         if (!merge) {  // the partial of an empty chunk is the merge identity
             RA_HIP(ra::launch_zero_f32(out, s));
@@ -225,31 +244,32 @@ ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_ten
         }
         return RA_OK;
     }
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_fwd_chunk_bf16(q, k, v, scale, out, lse, merge, s));
-    else RA_HIP(ra::launch_fwd_chunk_f32(q, k, v, scale, out, lse, merge, s));
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_fwd_chunk_bf16(q, k, v, km, scale, out, lse, merge, s));
+    else RA_HIP(ra::launch_fwd_chunk_f32(q, k, v, km, scale, out, lse, merge, s));
     return RA_OK;
 }
 
 ra_status enqueue_bwd_dkdv(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                           const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk,
-                           const ra_tensor& dv, hipStream_t s) {
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dkdv_bf16(q, k, v, dout, lse, delta, scale, dk, dv, s));
-    else RA_HIP(ra::launch_bwd_dkdv_f32(q, k, v, dout, lse, delta, scale, dk, dv, s));
+                           const ra_lse& lse, const ra_lse& delta, const ra::KeyMask& km, float scale,
+                           const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dkdv_bf16(q, k, v, dout, lse, delta, km, scale, dk, dv, s));
+    else RA_HIP(ra::launch_bwd_dkdv_f32(q, k, v, dout, lse, delta, km, scale, dk, dv, s));
     return RA_OK;
 }
 
 ra_status enqueue_bwd_dq(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                         const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq, hipStream_t s) {
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dq_bf16(q, k, v, dout, lse, delta, scale, dq, s));
-    else RA_HIP(ra::launch_bwd_dq_f32(q, k, v, dout, lse, delta, scale, dq, s));
+                         const ra_lse& lse, const ra_lse& delta, const ra::KeyMask& km, float scale,
+                         const ra_tensor& dq, hipStream_t s) {
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dq_bf16(q, k, v, dout, lse, delta, km, scale, dq, s));
+    else RA_HIP(ra::launch_bwd_dq_f32(q, k, v, dout, lse, delta, km, scale, dq, s));
     return RA_OK;
 }
 
 ra_status enqueue_bwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                            const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq,
-                            const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
-    RA_TRY(enqueue_bwd_dkdv(q, k, v, dout, lse, delta, scale, dk, dv, s));
-    RA_TRY(enqueue_bwd_dq(q, k, v, dout, lse, delta, scale, dq, s));
+                            const ra_lse& lse, const ra_lse& delta, const ra::KeyMask& km, float scale,
+                            const ra_tensor& dq, const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
+    RA_TRY(enqueue_bwd_dkdv(q, k, v, dout, lse, delta, km, scale, dk, dv, s));
+    RA_TRY(enqueue_bwd_dq(q, k, v, dout, lse, delta, km, scale, dq, s));
     return RA_OK;
 }
 
@@ -271,15 +291,21 @@ ra_status check_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tenso
 
 extern "C" {
 
-ra_status ra_fwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, float scale, ra_tensor* out,
-                       ra_lse* lse, int32_t merge, void* stream) {
+ra_status ra_fwd_chunk_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                              float scale, ra_tensor* out, ra_lse* lse, int32_t merge, void* stream) {
     RA_TRY(check_qkv(q, k, v));
     RA_TRY(check_acc(out, "out", *q));
     RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
     RA_TRY(check_scale(scale));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
     if (merge != 0 && merge != 1) return fail(RA_E_ARG, "merge must be 0 or 1");
-    RA_TRY(enqueue_fwd_chunk(*q, *k, *v, scale, *out, *lse, merge, (hipStream_t)stream));
+    RA_TRY(enqueue_fwd_chunk(*q, *k, *v, key_mask(kmask), scale, *out, *lse, merge, (hipStream_t)stream));
     return ok();
+}
+
+ra_status ra_fwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, float scale, ra_tensor* out,
+                       ra_lse* lse, int32_t merge, void* stream) {
+    return ra_fwd_chunk_masked(q, k, v, nullptr, scale, out, lse, merge, stream);
 }
 
 ra_status ra_merge_lse(ra_tensor* out_acc, ra_lse* lse_acc, const ra_tensor* out_part, const ra_lse* lse_part,
@@ -304,10 +330,12 @@ ra_status ra_bwd_delta(const ra_tensor* out, const ra_tensor* dout, ra_lse* delt
     return ok();
 }
 
-ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
-                       const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, ra_tensor* dk_acc,
-                       ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+ra_status ra_bwd_chunk_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                              const ra_lse* lse, const ra_lse* delta, const ra_kmask* kmask, float scale,
+                              ra_tensor* dq_acc, ra_tensor* dk_acc, ra_tensor* dv_acc, int32_t accumulate,
+                              void* stream) {
     RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
     RA_TRY(check_acc(dq_acc, "dq_acc", *q));
     RA_TRY(check_acc(dk_acc, "dk_acc", *k));
     RA_TRY(check_acc(dv_acc, "dv_acc", *k));
@@ -317,32 +345,55 @@ ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* 
         RA_HIP(ra::launch_zero_f32(*dk_acc, s));
         RA_HIP(ra::launch_zero_f32(*dv_acc, s));
     }
-    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_chunk(*q, *k, *v, *dout, *lse, *delta, scale, *dq_acc, *dk_acc, *dv_acc, s));
+    if (k->S > 0 && q->S > 0)
+        RA_TRY(enqueue_bwd_chunk(*q, *k, *v, *dout, *lse, *delta, key_mask(kmask), scale, *dq_acc, *dk_acc, *dv_acc, s));
+    return ok();
+}
+
+ra_status ra_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                       const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, ra_tensor* dk_acc,
+                       ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+    return ra_bwd_chunk_masked(q, k, v, dout, lse, delta, nullptr, scale, dq_acc, dk_acc, dv_acc, accumulate, stream);
+}
+
+ra_status ra_bwd_chunk_dkdv_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                                   const ra_lse* lse, const ra_lse* delta, const ra_kmask* kmask, float scale,
+                                   ra_tensor* dk_acc, ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
+    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
+    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
+    if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate) {
+        RA_HIP(ra::launch_zero_f32(*dk_acc, s));
+        RA_HIP(ra::launch_zero_f32(*dv_acc, s));
+    }
+    if (k->S > 0 && q->S > 0)
+        RA_TRY(enqueue_bwd_dkdv(*q, *k, *v, *dout, *lse, *delta, key_mask(kmask), scale, *dk_acc, *dv_acc, s));
     return ok();
 }
 
 ra_status ra_bwd_chunk_dkdv(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
                             const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dk_acc,
                             ra_tensor* dv_acc, int32_t accumulate, void* stream) {
+    return ra_bwd_chunk_dkdv_masked(q, k, v, dout, lse, delta, nullptr, scale, dk_acc, dv_acc, accumulate, stream);
+}
+
+ra_status ra_bwd_chunk_dq_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                                 const ra_lse* lse, const ra_lse* delta, const ra_kmask* kmask, float scale,
+                                 ra_tensor* dq_acc, void* stream) {
     RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
-    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
-    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
-    if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
-    hipStream_t s = (hipStream_t)stream;
-    if (!accumulate) {
-        RA_HIP(ra::launch_zero_f32(*dk_acc, s));
-        RA_HIP(ra::launch_zero_f32(*dv_acc, s));
-    }
-    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_dkdv(*q, *k, *v, *dout, *lse, *delta, scale, *dk_acc, *dv_acc, s));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
+    RA_TRY(check_acc(dq_acc, "dq_acc", *q));
+    if (k->S > 0 && q->S > 0)
+        RA_TRY(enqueue_bwd_dq(*q, *k, *v, *dout, *lse, *delta, key_mask(kmask), scale, *dq_acc, (hipStream_t)stream));
     return ok();
 }
 
 ra_status ra_bwd_chunk_dq(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
                           const ra_lse* lse, const ra_lse* delta, float scale, ra_tensor* dq_acc, void* stream) {
-    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
-    RA_TRY(check_acc(dq_acc, "dq_acc", *q));
-    if (k->S > 0 && q->S > 0) RA_TRY(enqueue_bwd_dq(*q, *k, *v, *dout, *lse, *delta, scale, *dq_acc, (hipStream_t)stream));
-    return ok();
+    return ra_bwd_chunk_dq_masked(q, k, v, dout, lse, delta, nullptr, scale, dq_acc, stream);
 }
 
 size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
@@ -368,9 +419,11 @@ static ra_status check_ws(void* ws, size_t ws_bytes, size_t need) {
     return RA_OK;
 }
 
-ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_chunks* chunks, float scale,
-                      ra_tensor* out, ra_lse* lse, void* ws, size_t ws_bytes, void* stream) {
+ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                             const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
     RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
     RA_TRY(check_tensor(out, "out"));
     if (!same_shape(*out, *q)) return fail(RA_E_SHAPE, "out must have the shape of q");
     RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
@@ -384,16 +437,23 @@ ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
         const int c = chunks->order[i];
         const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);
         const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
-        RA_TRY(enqueue_fwd_chunk(*q, kc, vc, scale, acc, *lse, i > 0 ? 1 : 0, s));
+        RA_TRY(enqueue_fwd_chunk(*q, kc, vc, key_mask(kmask, chunks->start[c]), scale, acc, *lse, i > 0 ? 1 : 0, s));
     }
     if (out->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(acc, *out, s));
     return ok();
 }
 
-ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
-                      const ra_tensor* dout, const ra_lse* lse, const ra_chunks* chunks, float scale, ra_tensor* dq,
-                      ra_tensor* dk, ra_tensor* dv, void* ws, size_t ws_bytes, void* stream) {
+ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_chunks* chunks, float scale,
+                      ra_tensor* out, ra_lse* lse, void* ws, size_t ws_bytes, void* stream) {
+    return ra_ring_fwd_masked(q, k, v, nullptr, chunks, scale, out, lse, ws, ws_bytes, stream);
+}
+
+ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
+                             const ra_tensor* dout, const ra_lse* lse, const ra_kmask* kmask, const ra_chunks* chunks,
+                             float scale, ra_tensor* dq, ra_tensor* dk, ra_tensor* dv, void* ws, size_t ws_bytes,
+                             void* stream) {
     RA_TRY(check_qkv(q, k, v));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
     RA_TRY(check_tensor(out, "out"));
     RA_TRY(check_tensor(dout, "dout"));
     if (!same_shape(*out, *q) || !same_shape(*dout, *q)) return fail(RA_E_SHAPE, "out and dout must have the shape of q");
@@ -429,12 +489,19 @@ ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
         const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
         const ra_tensor dkc = seq_slice(dk_acc, chunks->start[c], chunks->len[c]);
         const ra_tensor dvc = seq_slice(dv_acc, chunks->start[c], chunks->len[c]);
-        RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, scale, dq_acc, dkc, dvc, s));
+        RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, key_mask(kmask, chunks->start[c]), scale, dq_acc,
+                                 dkc, dvc, s));
     }
     if (dq->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));
     if (dk->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dk_acc, *dk, s));
     if (dv->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dv_acc, *dv, s));
     return ok();
+}
+
+ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* out,
+                      const ra_tensor* dout, const ra_lse* lse, const ra_chunks* chunks, float scale, ra_tensor* dq,
+                      ra_tensor* dk, ra_tensor* dv, void* ws, size_t ws_bytes, void* stream) {
+    return ra_ring_bwd_masked(q, k, v, out, dout, lse, nullptr, chunks, scale, dq, dk, dv, ws, ws_bytes, stream);
 }
 
 ra_status ra_seq_head_permute(const ra_tensor* in, int32_t n_in, ra_tensor* out, int32_t n_out, int32_t dir,

@@ -21,6 +21,13 @@ constexpr int kBwdBlockM = 64;                            // query rows per LDS 
 
 constexpr int kMaxRanks = 16;  // exchange fan-out limit (kernel argument table)
 
+// Key mask of one chunk as the kernels see it: data[b * sB + key] != 0 means the key
+// takes part; data == nullptr means every key does.
+struct KeyMask {
+    const uint8_t* data;
+    int64_t sB;
+};
+
 struct PermuteTable {
     int32_t n_in, n_out, dir, elem_bytes;
     ra_tensor in[kMaxRanks];
@@ -31,24 +38,24 @@ struct PermuteTable {
 
 // All launchers enqueue on `s` and return hipGetLastError() of the launch.
 // Shapes have been validated by the caller.
-hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
-                                 const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
-hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, float scale,
-                                const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
+hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
+                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
+hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
+                                float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
 // Backward chunk step, split: add this chunk's contribution to dk_acc/dv_acc, or to
 // dq_acc (all fp32).
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                                const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
-                                const ra_tensor& dv_acc, hipStream_t s);
+                                const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                              const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                              hipStream_t s);
+                              const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                              const ra_tensor& dq_acc, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                               const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dk_acc,
-                               const ra_tensor& dv_acc, hipStream_t s);
+                               const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                               const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
-                             const ra_lse& lse, const ra_lse& delta, float scale, const ra_tensor& dq_acc,
-                             hipStream_t s);
+                             const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
+                             const ra_tensor& dq_acc, hipStream_t s);
 hipError_t launch_merge_lse(const ra_tensor& out_acc, const ra_lse& lse_acc, const ra_tensor& out_part,
                             const ra_lse& lse_part, hipStream_t s);
 hipError_t launch_bwd_delta(const ra_tensor& out, const ra_tensor& dout, const ra_lse& delta, hipStream_t s);

@@ -12,7 +12,7 @@ import math
 import torch
 
 from . import _abi
-from ._abi import RaChunks, RaLse, RaTensor, check, lib
+from ._abi import RaChunks, RaKMask, RaLse, RaTensor, check, lib
 
 _DT = {torch.bfloat16: _abi.RA_BF16, torch.float32: _abi.RA_F32}
 
@@ -46,6 +46,18 @@ def rows_desc(t):
     if t.dim() != 3 or t.dtype != torch.float32 or (t.numel() > 0 and t.stride(2) != 1):
         raise ValueError("row statistics are fp32 [B, H, S] with S contiguous")
     return RaLse(t.data_ptr(), t.shape[0], t.shape[1], t.shape[2], t.stride(0), t.stride(1))
+
+
+def kmask_desc(m):
+    """Key-validity mask [B, S_k] (bool or uint8 on the GPU, S contiguous; nonzero = the key
+    takes part), or None."""
+    if m is None:
+        return None
+    if m.dim() != 2 or m.dtype not in (torch.bool, torch.uint8) or (m.numel() > 0 and m.stride(1) != 1):
+        raise ValueError("kmask is a bool/uint8 [B, S_k] tensor with S contiguous")
+    if not m.is_cuda:
+        raise ValueError("kmask must be on the GPU")
+    return ctypes.byref(RaKMask(m.data_ptr(), m.shape[0], m.shape[1], m.stride(0)))
 
 
 def _stream(t):
@@ -90,11 +102,16 @@ class Chunks:
         return len(self.lens)
 
 
-def fwd_chunk(q, k, v, out, lse, merge, scale=None, layout="bshd"):
+def fwd_chunk(q, k, v, out, lse, merge, scale=None, layout="bshd", kmask=None):
     _dev_check(q, k, v, out, lse)
     dq, dk, dv, do = (tensor_desc(x, layout) for x in (q, k, v, out))
     dl = rows_desc(lse)
-    check(lib().ra_fwd_chunk(dq, dk, dv, _scale(scale, q.shape[-1]), do, dl, int(merge), _stream(q)), "ra_fwd_chunk")
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_fwd_chunk(dq, dk, dv, sc, do, dl, int(merge), _stream(q)), "ra_fwd_chunk")
+    else:
+        check(lib().ra_fwd_chunk_masked(dq, dk, dv, kmask_desc(kmask), sc, do, dl, int(merge), _stream(q)),
+              "ra_fwd_chunk_masked")
 
 
 def merge_lse(out_acc, lse_acc, out_part, lse_part, layout="bshd"):
@@ -109,27 +126,42 @@ def bwd_delta(out, dout, delta, layout="bshd"):
           "ra_bwd_delta")
 
 
-def bwd_chunk(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, accumulate, scale=None, layout="bshd"):
+def bwd_chunk(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, accumulate, scale=None, layout="bshd", kmask=None):
     _dev_check(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc)
     d = [tensor_desc(x, layout) for x in (q, k, v, dout)]
     a = [tensor_desc(x, layout) for x in (dq_acc, dk_acc, dv_acc)]
-    check(lib().ra_bwd_chunk(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), _scale(scale, q.shape[-1]),
-                             a[0], a[1], a[2], int(accumulate), _stream(q)), "ra_bwd_chunk")
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_bwd_chunk(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), sc,
+                                 a[0], a[1], a[2], int(accumulate), _stream(q)), "ra_bwd_chunk")
+    else:
+        check(lib().ra_bwd_chunk_masked(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), kmask_desc(kmask), sc,
+                                        a[0], a[1], a[2], int(accumulate), _stream(q)), "ra_bwd_chunk_masked")
 
 
-def bwd_chunk_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, accumulate, scale=None, layout="bshd"):
+def bwd_chunk_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, accumulate, scale=None, layout="bshd", kmask=None):
     _dev_check(q, k, v, dout, lse, delta, dk_acc, dv_acc)
     d = [tensor_desc(x, layout) for x in (q, k, v, dout, dk_acc, dv_acc)]
-    check(lib().ra_bwd_chunk_dkdv(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
-                                  _scale(scale, q.shape[-1]), d[4], d[5], int(accumulate), _stream(q)),
-          "ra_bwd_chunk_dkdv")
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_bwd_chunk_dkdv(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), sc, d[4], d[5],
+                                      int(accumulate), _stream(q)), "ra_bwd_chunk_dkdv")
+    else:
+        check(lib().ra_bwd_chunk_dkdv_masked(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
+                                             kmask_desc(kmask), sc, d[4], d[5], int(accumulate), _stream(q)),
+              "ra_bwd_chunk_dkdv_masked")
 
 
-def bwd_chunk_dq(q, k, v, dout, lse, delta, dq_acc, scale=None, layout="bshd"):
+def bwd_chunk_dq(q, k, v, dout, lse, delta, dq_acc, scale=None, layout="bshd", kmask=None):
     _dev_check(q, k, v, dout, lse, delta, dq_acc)
     d = [tensor_desc(x, layout) for x in (q, k, v, dout, dq_acc)]
-    check(lib().ra_bwd_chunk_dq(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
-                                _scale(scale, q.shape[-1]), d[4], _stream(q)), "ra_bwd_chunk_dq")
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_bwd_chunk_dq(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), sc, d[4], _stream(q)),
+              "ra_bwd_chunk_dq")
+    else:
+        check(lib().ra_bwd_chunk_dq_masked(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta),
+                                           kmask_desc(kmask), sc, d[4], _stream(q)), "ra_bwd_chunk_dq_masked")
 
 
 def _rows_shape(q, layout):
@@ -140,11 +172,13 @@ def _rows_shape(q, layout):
     return (B, H, S)
 
 
-def ring_fwd(q, k, v, chunks, scale=None, out=None, lse=None, out_dtype=None, layout="bshd", workspace=None):
+def ring_fwd(q, k, v, chunks, scale=None, out=None, lse=None, out_dtype=None, layout="bshd", workspace=None,
+             kmask=None):
     """Sweep the local query shard q over every chunk of (k, v) in ``chunks.order``.
 
     Returns (out, lse); out has q's layout and ``out_dtype`` (default q.dtype), lse is
-    fp32 [B, H_q, S_q].
+    fp32 [B, H_q, S_q].  ``kmask``: optional key-validity mask [B, S_k] of the whole
+    key sequence (nonzero = the key takes part).
     """
     _dev_check(q, k, v)
     if not isinstance(chunks, Chunks):
@@ -156,15 +190,21 @@ def ring_fwd(q, k, v, chunks, scale=None, out=None, lse=None, out_dtype=None, la
     tq, tk, tv, to = (tensor_desc(x, layout) for x in (q, k, v, out))
     need = lib().ra_ring_fwd_workspace_bytes(tq, to)
     ws = _workspace(workspace, need, q.device)
-    check(lib().ra_ring_fwd(tq, tk, tv, ctypes.byref(chunks.c), _scale(scale, q.shape[-1]), to, rows_desc(lse),
-                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), need, _stream(q)), "ra_ring_fwd")
+    wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_ring_fwd(tq, tk, tv, ctypes.byref(chunks.c), sc, to, rows_desc(lse), wsp, need, _stream(q)),
+              "ra_ring_fwd")
+    else:
+        check(lib().ra_ring_fwd_masked(tq, tk, tv, kmask_desc(kmask), ctypes.byref(chunks.c), sc, to, rows_desc(lse),
+                                       wsp, need, _stream(q)), "ra_ring_fwd_masked")
     return out, lse
 
 
 def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layout="bshd", workspace=None,
-             dq=None, dk=None, dv=None):
+             dq=None, dk=None, dv=None, kmask=None):
     """Backward sweep in the forward's chunk order; returns (dq, dk, dv) (written into
-    dq/dk/dv when given)."""
+    dq/dk/dv when given).  ``kmask``: the forward's key-validity mask, if any."""
     _dev_check(q, k, v, out, dout, lse)
     if not isinstance(chunks, Chunks):
         chunks = Chunks(chunks)
@@ -175,9 +215,15 @@ def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layou
     t = [tensor_desc(x, layout) for x in (q, k, v, out, dout, dq, dk, dv)]
     need = lib().ra_ring_bwd_workspace_bytes(t[0], t[1], t[5], t[6], t[7])
     ws = _workspace(workspace, need, q.device)
-    check(lib().ra_ring_bwd(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), ctypes.byref(chunks.c),
-                            _scale(scale, q.shape[-1]), t[5], t[6], t[7],
-                            ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), need, _stream(q)), "ra_ring_bwd")
+    wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    sc = _scale(scale, q.shape[-1])
+    if kmask is None:
+        check(lib().ra_ring_bwd(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), ctypes.byref(chunks.c), sc,
+                                t[5], t[6], t[7], wsp, need, _stream(q)), "ra_ring_bwd")
+    else:
+        check(lib().ra_ring_bwd_masked(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), kmask_desc(kmask),
+                                       ctypes.byref(chunks.c), sc, t[5], t[6], t[7], wsp, need, _stream(q)),
+              "ra_ring_bwd_masked")
     return dq, dk, dv
 
 

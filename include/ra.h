@@ -39,8 +39,10 @@
  * GQA: H_kv must divide H_q; query head h uses key/value head h / (H_q/H_kv).
  * Scale: the softmax scale is an argument; the Python binding passes
  *   1/sqrt(D) (the SDPA default of [P1] "Reproduction") when none is given.
- *   There is no mask, dropout or causal mode ([P4] "Testcase" calls attention
- *   with None, 0.0, False); none is offered, so none can be silently ignored.
+ *   There is no dropout, causal mode or general attention mask ([P4]
+ *   "Testcase" calls attention with None, 0.0, False); none is offered, so
+ *   none can be silently ignored.  The one mask offered is a key-validity
+ *   (key-padding) mask, through the *_masked entry points below.
  * Errors: each call validates all arguments on the host BEFORE any launch and
  *   returns a status; on failure nothing has been enqueued and ra_last_error()
  *   describes the problem.  Anything the library cannot compute exactly is
@@ -102,6 +104,22 @@ typedef struct {
     const int32_t* order;
 } ra_chunks;
 
+/* Key-validity mask of a key sequence (key padding): key s of batch b takes part
+ * in attention iff data[b*sB + s] != 0.  uint8 in device memory, S contiguous.
+ * [P3] (comments on padding to a length divisible by the world size): padded
+ * tokens change the result because they are attended, and masking them is the
+ * way to keep padded inputs exact.  Masked keys leave every softmax of their
+ * batch; a query row of a batch with no valid key in the swept keys gets
+ * out = 0, lse = -inf and zero gradients; masked keys get dK = dV = 0.
+ * Where a *_masked entry point takes k as a chunk, the mask covers that chunk
+ * (S = its S_k); for the ring sweeps it covers the whole key sequence and is
+ * sliced with the chunks.  A NULL mask pointer means no mask. */
+typedef struct {
+    const uint8_t* data;
+    int32_t B, S;
+    int64_t sB;
+} ra_kmask;
+
 /* ---------------------------------------------------------------- chunk steps */
 
 /* One forward chunk step ([P1] "Root cause": per ring iteration the attention
@@ -153,6 +171,23 @@ ra_status ra_bwd_chunk_dq(const ra_tensor* q, const ra_tensor* k, const ra_tenso
                           const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
                           float scale, ra_tensor* dq_acc, void* stream);
 
+/* The chunk steps with a key mask (kmask may be NULL: same as the entry points
+ * above).  kmask covers the chunk k: B = q.B, S = k.S. */
+ra_status ra_fwd_chunk_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                              const ra_kmask* kmask, float scale, ra_tensor* out, ra_lse* lse,
+                              int32_t merge, void* stream);
+ra_status ra_bwd_chunk_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                              const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                              const ra_kmask* kmask, float scale, ra_tensor* dq_acc,
+                              ra_tensor* dk_acc, ra_tensor* dv_acc, int32_t accumulate, void* stream);
+ra_status ra_bwd_chunk_dkdv_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                                   const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                                   const ra_kmask* kmask, float scale, ra_tensor* dk_acc,
+                                   ra_tensor* dv_acc, int32_t accumulate, void* stream);
+ra_status ra_bwd_chunk_dq_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                                 const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                                 const ra_kmask* kmask, float scale, ra_tensor* dq_acc, void* stream);
+
 /* ---------------------------------------------------------------- ring sweeps */
 
 /* Forward sweep of the local query shard over every chunk in chunks->order:
@@ -175,6 +210,17 @@ ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
                       const ra_chunks* chunks, float scale,
                       ra_tensor* dq, ra_tensor* dk, ra_tensor* dv,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* The ring sweeps with a key mask over the whole key sequence (B = q.B,
+ * S = k.S; sliced with the chunks).  kmask may be NULL.  Workspaces as above. */
+ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                             const ra_kmask* kmask, const ra_chunks* chunks, float scale,
+                             ra_tensor* out, ra_lse* lse, void* ws, size_t ws_bytes, void* stream);
+ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                             const ra_tensor* out, const ra_tensor* dout, const ra_lse* lse,
+                             const ra_kmask* kmask, const ra_chunks* chunks, float scale,
+                             ra_tensor* dq, ra_tensor* dk, ra_tensor* dv,
+                             void* ws, size_t ws_bytes, void* stream);
 
 size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out);
 size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k,

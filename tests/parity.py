@@ -39,7 +39,7 @@ def max_abs(got, ref):
     return float(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)).max())
 
 
-def oracle_by_head(q, k, v, dout, heads, scale=None, backward=True, row_block=512):
+def oracle_by_head(q, k, v, dout, heads, scale=None, backward=True, row_block=512, kmask=None):
     """Oracle forward (and backward) restricted to query heads ``heads`` of a
     [B,S,H,D] problem, one thread per head.  Returns dict with out/lse/dq for
     those heads (head axis in the order given) and dk/dv summed per kv head
@@ -50,10 +50,11 @@ def oracle_by_head(q, k, v, dout, heads, scale=None, backward=True, row_block=51
     def one(h):
         g = h // G
         qs, ks, vs = q[:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1]
-        o, l = oracle.attention_forward(qs, ks, vs, scale=scale, row_block=row_block)
+        o, l = oracle.attention_forward(qs, ks, vs, scale=scale, row_block=row_block, kmask=kmask)
         res = {"out": o[:, :, 0], "lse": l[:, 0]}
         if backward:
-            dq, dk, dv = oracle.attention_backward(qs, ks, vs, dout[:, :, h:h + 1], scale=scale, row_block=row_block)
+            dq, dk, dv = oracle.attention_backward(qs, ks, vs, dout[:, :, h:h + 1], scale=scale, row_block=row_block,
+                                                   kmask=kmask)
             res.update(dq=dq[:, :, 0], dk=dk[:, :, 0], dv=dv[:, :, 0], g=g)
         return res
 

@@ -207,3 +207,41 @@ def test_status_strings():
     lib = _lib()
     for i, name in enumerate(abi.STATUS_NAMES):
         assert lib.ra_status_string(i).decode() == name
+
+
+# ------------------------------------------------------------------ key mask (no launch)
+def K(B, S, data=FAKE, sB=None):
+    return abi.RaKMask(data, B, S, S if sB is None else sB)
+
+
+@pytest.mark.parametrize("case, status", [
+    ("batch", abi.RA_E_SHAPE), ("keys", abi.RA_E_SHAPE), ("null_data", abi.RA_E_ARG),
+    ("neg_stride", abi.RA_E_ARG), ("rows_overlap", abi.RA_E_ARG),
+])
+def test_masked_entry_points_refuse_bad_masks(case, status):
+    lib = _lib()
+    B, Sq, Sk = 2, 64, 96
+    q, k, v, o, l = T(B, Sq, 8, 64), T(B, Sk, 8, 64), T(B, Sk, 8, 64), T(B, Sq, 8, 64, abi.RA_F32), Lrows(B, 8, Sq)
+    m = K(B, Sk)
+    if case == "batch": m.B = 1
+    if case == "keys": m.S = Sk - 1
+    if case == "null_data": m.data = None
+    if case == "neg_stride": m.sB = -Sk
+    if case == "rows_overlap": m.sB = Sk - 1
+    assert lib.ra_fwd_chunk_masked(q, k, v, ctypes.byref(m), 0.125, o, l, 0, None) == status, lib.ra_last_error()
+    c = chunks([48, 48], [1, 0])
+    assert lib.ra_ring_fwd_masked(q, k, v, ctypes.byref(m), ctypes.byref(c), 0.125, o, l, None, 0, None) == status
+    acc = T(B, Sq, 8, 64, abi.RA_F32)
+    kacc = T(B, Sk, 8, 64, abi.RA_F32)
+    st = lib.ra_bwd_chunk_masked(q, k, v, q, l, l, ctypes.byref(m), 0.125, acc, kacc, kacc, 1, None)
+    assert st == status
+    assert lib.ra_bwd_chunk_dq_masked(q, k, v, q, l, l, ctypes.byref(m), 0.125, acc, None) == status
+    assert lib.ra_bwd_chunk_dkdv_masked(q, k, v, q, l, l, ctypes.byref(m), 0.125, kacc, kacc, 1, None) == status
+
+
+def test_masked_entry_points_validate_the_rest_as_before():
+    """A NULL mask is no mask: the masked entry points refuse exactly what the plain ones do."""
+    lib = _lib()
+    q, k, v, o, l = good(Hq=6, Hkv=4)
+    assert lib.ra_fwd_chunk_masked(q, k, v, None, 0.125, o, l, 0, None) == abi.RA_E_SHAPE
+    assert golden()["gqa_divisibility_error"]["message"] in lib.ra_last_error().decode()

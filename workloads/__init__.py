@@ -88,3 +88,22 @@ def randn(shape, seed, dtype="f32", mult=1.0):
     if mult != 1.0:
         t = t * mult
     return t.to(torch_dtype(dtype))
+
+
+def make_key_mask(B, S, seed, p_keep=0.8, valid_len=None, masked_ranges=()):
+    """Seeded key-validity mask [B, S] (bool, True = the key takes part), CPU.
+
+    Each key is kept with probability ``p_keep`` (independent draws from a CPU
+    ``torch.Generator`` seeded with ``seed``); ``valid_len[b]`` additionally masks
+    keys >= valid_len[b] of batch b (right padding, as a padded text sequence would
+    have); ``masked_ranges`` is a list of (b, start, stop) key ranges masked as a
+    whole.  Shapes and random numbers only.
+    """
+    g = torch.Generator().manual_seed(seed)
+    m = torch.rand((B, S), generator=g) < p_keep
+    if valid_len is not None:
+        for b, n in enumerate(valid_len):
+            m[b, int(n):] = False
+    for b, a, z in masked_ranges:
+        m[b, a:z] = False
+    return m

@@ -76,8 +76,10 @@ def setup(Sq_rows, full):
 MASK_RECIPE = dict(p_keep=0.95, valid_len=(30000,))  # right padding past 30000 keys + 5 % random holes
 
 
-def run_workload(full, steps, warmup, masked=False):
+def run_workload(full, steps, warmup, masked=False, single=False):
     w, lens, order, q, k, v, do = setup(4096, full)
+    if single:  # all-gather variant: one fused sweep over the resident key sequence
+        lens, order = [w.S], [0]
     ch = ra.Chunks(lens, order)
     km = W.make_key_mask(w.B, w.S, 990, **MASK_RECIPE).to(q.device) if masked else None
     out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
@@ -188,6 +190,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip the full-Q sweep (extra field)")
     ap.add_argument("--no-masked", action="store_true", help="skip the key-masked sweep (extra field)")
+    ap.add_argument("--no-allgather", action="store_true", help="skip the single fused sweep (extra field)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only launch the dominant kernel (for hardware-counter runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -269,6 +272,16 @@ def main():
                          "fwd_tflops": round(rm["f_f"] / rm["t_fwd"] / 1e12, 2),
                          "bwd_tflops": round(rm["f_b"] / rm["t_bwd"] / 1e12, 2)}
         del rm
+        torch.cuda.empty_cache()
+    if not args.no_allgather:
+        ra_ = run_workload(False, max(3, args.steps // 2), 1, single=True)
+        ta = ra_["f_f"] + ra_["f_b"]
+        res["allgather"] = {"chunks": [ra_["w"].S], "ms_per_step": round(ra_["t_step"] * 1e3, 3),
+                            "tflops": round(ta / ra_["t_step"] / 1e12, 2),
+                            "pct_of_peak": round(100.0 * ta / ra_["t_step"] / 1e12 / PEAK_BF16_TFLOPS, 2),
+                            "fwd_tflops": round(ra_["f_f"] / ra_["t_fwd"] / 1e12, 2),
+                            "bwd_tflops": round(ra_["f_b"] / ra_["t_bwd"] / 1e12, 2)}
+        del ra_
         torch.cuda.empty_cache()
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     print(json.dumps(res), flush=True)

@@ -6,5 +6,7 @@ The computation lives in ``libra.so`` (HIP kernels for gfx950 behind the C ABI o
 from .ops import (Chunks, bwd_chunk, bwd_chunk_dkdv, bwd_chunk_dq, bwd_delta, fwd_chunk, head_to_seq, merge_lse, ring_bwd, ring_fwd,
                   ring_order, rows_desc, seq_head_permute, seq_to_head, split_sizes, tensor_desc)
 
-__all__ = ["Chunks", "bwd_chunk", "bwd_chunk_dkdv", "bwd_chunk_dq", "bwd_delta", "fwd_chunk", "head_to_seq", "merge_lse", "ring_bwd", "ring_fwd",
+from .autograd import head_to_seq_exchange, ring_attention, seq_to_head_exchange
+
+__all__ = ["ring_attention", "seq_to_head_exchange", "head_to_seq_exchange", "Chunks", "bwd_chunk", "bwd_chunk_dkdv", "bwd_chunk_dq", "bwd_delta", "fwd_chunk", "head_to_seq", "merge_lse", "ring_bwd", "ring_fwd",
            "ring_order", "rows_desc", "seq_head_permute", "seq_to_head", "split_sizes", "tensor_desc"]

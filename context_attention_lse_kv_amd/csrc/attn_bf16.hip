@@ -502,9 +502,15 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         vo[i] = copy_voff<D>(w * NI + i, lane, p.do_sS);
     }
     float lpre = 0.f, dpre = 0.f;
-    // tile it: Q tile it % ntq of query head g G + it / ntq, into buffer it % 3
-    auto issue = [&](int it, int buf) {
-        const int hq = g * p.G + it / ntq, r0 = (it % ntq) * BM;
+    // Tiles are copied in order: tile it is Q tile it % ntq of query head g G + it / ntq,
+    // tracked incrementally (no division per tile) by (iss_h, iss_t).
+    int iss_h = g * p.G, iss_t = 0;
+    auto issue = [&](int buf) {
+        const int hq = iss_h, r0 = iss_t * BM;
+        if (++iss_t == ntq) {
+            iss_t = 0;
+            ++iss_h;
+        }
         const uint16_t* qbase = p.q + (int64_t)b * p.q_sB + (int64_t)hq * p.q_sH;
         const uint16_t* obase = p.dout + (int64_t)b * p.do_sB + (int64_t)hq * p.do_sH;
         const i32x4_t rq = tile_desc(qbase, r0, p.q_sS * 2, p.q_bytes);
@@ -563,10 +569,10 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     for (int rb = 0; rb < RB; ++rb) sacc[rb] = f32x16_t{};
 
     __syncthreads();  // LDS zeroed
-    issue(0, 0);
+    issue(0);
     wait_vmem();
     commit_stats(0);
-    if (ntiles > 1) issue(1, 1);
+    if (ntiles > 1) issue(1);
     __syncthreads();
     int cur = 0;  // buffer of tile t; tile t-1 sits in (cur + 2) % 3
     for (int it = 0; it <= ntiles; ++it) {
@@ -659,7 +665,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
             commit_stats(nxt);
         }
         __syncthreads();
-        if (it + 2 < ntiles) issue(it + 2, prv);
+        if (it + 2 < ntiles) issue(prv);  // tile it + 2
         cur = nxt;
     }
 

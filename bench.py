@@ -72,8 +72,7 @@ def run_workload(full, steps, warmup, masked=False, single=False):
     dq, dk, dv = (torch.empty(t.shape, dtype=torch.bfloat16, device=q.device) for t in (q, k, v))
     # workspaces allocated once, outside the timed region
     fws = torch.empty(q.numel() * 4 + 256, dtype=torch.uint8, device=q.device)
-    bws = torch.empty(w.B * w.Hq * q.shape[1] * 4 + (q.numel() + 2 * k.numel()) * 4 + 4096, dtype=torch.uint8,
-                      device=q.device)
+    bws = torch.empty(ra.ring_bwd_workspace_bytes(q, k), dtype=torch.uint8, device=q.device)
 
     def fwd():
         ra.ring_fwd(q, k, v, ch, out=out, lse=lse, workspace=fws, kmask=km)

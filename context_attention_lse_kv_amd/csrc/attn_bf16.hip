@@ -77,6 +77,10 @@ struct BwdParams {
     float scale, c;
     const uint8_t* km;  // key mask of the chunk (km[b * km_sB + key] != 0: key takes part), or null
     int64_t km_sB;
+    // dS workspace (bf16): one 4 KiB block per (batch, query head, 32-key group, 64-row
+    // query tile), ds_nkg groups x ds_nqt tiles per (batch, query head); null = none
+    uint16_t* ds;
+    int ds_nqt, ds_nkg;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -478,6 +482,10 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     const int n0 = kt * BN;
     const int key = n0 + 32 * kg + l32;  // this lane's key (column of S/dP, row of dK/dV)
     const bool keys_partial = n0 + BN > p.Sk;
+    // a key past the chunk or masked out takes no part in dQ: its stored dS is zero
+    const bool ds_zap = keys_partial || p.km != nullptr;
+    uint32_t ds_keep = key < p.Sk ? ~0u : 0u;
+    if (p.km && load_key_byte(p.km + (int64_t)b * p.km_sB, p.Sk, n0 + 32 * kg, l32) == 0) ds_keep = 0u;
     const int ntq = (p.Sq + BM - 1) / BM;  // Q tiles per query head
     const int ntiles = ntq * p.G;          // every Q tile of every query head of the group
 
@@ -575,6 +583,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     if (ntiles > 1) issue(1);
     __syncthreads();
     int cur = 0;  // buffer of tile t; tile t-1 sits in (cur + 2) % 3
+    int ds_h = g * p.G, ds_t = 0;  // query head and 64-row tile of tile t-1 (dS store)
     for (int it = 0; it <= ntiles; ++it) {
         const int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
         const RA_LDS char* rowb = lbase + 2 * cur * TILEB + own_off;
@@ -604,6 +613,26 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                         pk[rb][t2][2 * u + 1] = pack_bf16x2(dsv[2], dsv[3]);
                     }
                 }
+            if (p.ds != nullptr && it > 0) {
+                // dS of tile t-1 for the dQ pass: block (head, 32-key group, tile), sub-block
+                // grp = 16-row group, then key row (32 B: the lane pair's two 16-byte packs).
+                // Non-temporal: the stream must not push the Q/dO tiles out of L2.
+                char* blk = (char*)p.ds +
+                            ((((int64_t)b * p.Hq + ds_h) * p.ds_nkg + n0 / 32 + kg) * p.ds_nqt + ds_t) * 4096 +
+                            l32 * 32 + hh * 16;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2) {
+                        u32x4_t v = pk[rb][t2];
+                        if (ds_zap) v = u32x4_t{v[0] & ds_keep, v[1] & ds_keep, v[2] & ds_keep, v[3] & ds_keep};
+                        __builtin_nontemporal_store(v, (u32x4_t*)(blk + (2 * rb + t2) * 1024));
+                    }
+                if (++ds_t == ntq) {
+                    ds_t = 0;
+                    ++ds_h;
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -874,6 +903,164 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
         }
 }
 
+// ------------------------------------------------------- dQ from the stored dS (Q-stationary)
+// dQ = scale dS K with the dS blocks the dK/dV kernel wrote, so S and dP are not formed a
+// second time.  Workgroup = kDqsWaves wavefronts x one 64-row query tile each, of one query
+// head; sweeps the chunk's keys in tiles of 32 (one dS block per wavefront and tile; the
+// workgroup's blocks of a tile are adjacent in memory)
+// through a ring of kDqsStages LDS stages, so that three tiles are in flight while one is
+// used: the kernel is bound by reading dS from HBM.  dQ^T += K^T dS^T takes both operands
+// with transposing reads (K^T like V^T in the forward; dS^T from the key-major blocks).
+// The operands' shared k index runs over the 16 keys of a step in the order 4 hh + (0..3),
+// 8 + 4 hh + (0..3) for lane half hh, as in the forward.
+//   A dS block's 16-byte chunk c = 64 grp + 2 key + hh holds dS[key][8 hh .. 8 hh + 7] of
+// the 16-row group grp in the lane order of the dK/dV kernel's A operand: entry 8 hh + i
+// is query row 16 grp + 4 hh + (i & 3) + 8 (i >> 2), i.e. bits 2 and 3 of the row index
+// swapped.  In LDS the four-key quads of odd groups are swapped pairwise (chunk
+// c ^ 8 (grp & 1)) so that the four 16-lane quarters of a transposing read cover both
+// halves of the banks.
+constexpr int kDqsStages = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdParams p) {
+    constexpr int DB = D / 32, BN = 32;
+    constexpr int RC = D / 8, ROWB = D * 2, KTB = BN * ROWB;
+    constexpr int KCOPIES = KTB / 1024;                        // wavefront-wide copies per K tile
+    static_assert(RC >= 8 && KCOPIES >= 1 && KCOPIES <= kDqsWaves, "tile geometry");
+    constexpr int STB = KTB + kDqsWaves * 4096;                // stage: [K tile | dS block of wave 0 .. 7]
+    __shared__ __attribute__((aligned(1024))) char smem[kDqsStages * STB];
+    RA_LDS char* const lbase = (RA_LDS char*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, l32 = lane & 31;
+    const int gq = lane >> 4, l16 = lane & 15, e4 = l16 >> 2, a4 = l16 & 3;
+    const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int qb = (int)(logical % p.n_tiles);
+    const int rest = (int)(logical / p.n_tiles);
+    const int h = rest % p.Hq, b = rest / p.Hq, g = h / p.G;
+    const int qt = qb * kDqsWaves + w;  // this wavefront's 64-row query tile
+    const bool copies_k = w < KCOPIES;   // uniform per wavefront
+
+    // this wavefront's dS blocks (key group it, tile qt) at (it ds_nqt + qt) of the (batch,
+    // head) slab, so that a workgroup's wavefronts read adjacent blocks.  A tile at or past
+    // ds_nqt (rows past the end, never stored) reads another group's block or, past the
+    // slab, zeros.
+    const int64_t slab_blocks = (int64_t)p.ds_nqt * p.ds_nkg;
+    const char* slab = (const char*)p.ds + ((int64_t)b * p.Hq + h) * slab_blocks * 4096;
+    const int64_t slab_bytes = slab_blocks * 4096;
+    uint32_t vds[4];  // copy offsets: LDS chunk 64 i + lane <- block chunk (64 i + lane) ^ 8 (i & 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vds[i] = (uint32_t)(((64 * i + lane) ^ (8 * (i & 1))) * 16);
+
+    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
+    const uint32_t vk = copy_voff<D>(w, lane, p.k_sS);
+    // tile it (keys 32 it ..) into stage it % kDqsStages: one K copy (first KCOPIES
+    // wavefronts) and the wavefront's own dS block
+    auto issue = [&](int it) {
+        RA_LDS char* st = lbase + (it % kDqsStages) * STB;
+        if (copies_k) dma16(tile_desc(kbase, (int64_t)it * BN, p.k_sS * 2, p.k_bytes), st + w * 1024, vk);
+        const int64_t off = ((int64_t)it * p.ds_nqt + qt) * 4096;
+        const i32x4_t rd = make_desc(slab + off, off < slab_bytes ? (uint32_t)(slab_bytes - off) : 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(rd, st + KTB + w * 4096 + i * 1024, vds[i]);
+    };
+    // lane-constant LDS offsets: K^T reads (as V^T in the forward) and dS^T reads
+    const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
+    int tr_off[DB], tr_off8[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+        tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
+    }
+    // dS^T operand of query block qr (32 rows = groups 2 qr, 2 qr + 1), keys 16 t + (0..15):
+    // quarter gq reads group 2 qr + (gq & 1), keys 16 t + 4 hh + e4 and 16 t + 8 + 4 hh + e4,
+    // columns 4 a4 .. 4 a4 + 3
+    auto ds_off = [&](int qr, int key) {
+        const int grp = 2 * qr + (gq & 1);
+        return grp * 1024 + ((((key >> 2) ^ (grp & 1)) * 8 + (key & 3) * 2 + (a4 >> 1)) * 16) + 8 * (a4 & 1);
+    };
+    int dso[2][2][2];  // [query block][key step][first / second read]
+#pragma unroll
+    for (int qr = 0; qr < 2; ++qr)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            dso[qr][t][0] = ds_off(qr, 16 * t + 4 * hh + e4);
+            dso[qr][t][1] = ds_off(qr, 16 * t + 8 + 4 * hh + e4);
+        }
+
+    f32x16_t acc[2][DB];
+#pragma unroll
+    for (int qr = 0; qr < 2; ++qr)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qr][db] = f32x16_t{};
+
+    const int ntiles = (p.Sk + BN - 1) / BN;
+#pragma unroll
+    for (int i = 0; i < kDqsStages - 1; ++i)
+        if (i < ntiles) issue(i);
+    for (int it = 0; it < ntiles; ++it) {
+        // tile it has landed once at most the copies of the (up to two) later tiles
+        // issued so far are outstanding: 4 dS copies + 1 K copy per tile and wavefront
+        const int later = min(ntiles - 1 - it, kDqsStages - 2);
+        if (copies_k) {
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 5);
+            else wait_vmem();
+        } else {
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+            else wait_vmem();
+        }
+        // after the barrier every wavefront's part of tile it is visible and the stage of
+        // tile it - 1 is free again
+        __syncthreads();
+        if (it + kDqsStages - 1 < ntiles) issue(it + kDqsStages - 1);
+        const RA_LDS char* kb = lbase + (it % kDqsStages) * STB;
+        const RA_LDS char* dsb = kb + KTB + w * 4096;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {  // 16 keys 16 t .. 16 t + 15 of the tile
+            u32x2_t kf[DB][2], df[2][2];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                kf[db][0] = lds_tr((const lds_u16*)(kb + 16 * t * ROWB + tr_off[db]));
+                kf[db][1] = lds_tr((const lds_u16*)(kb + (16 * t + 8) * ROWB + tr_off8[db]));
+            }
+#pragma unroll
+            for (int qr = 0; qr < 2; ++qr) {
+                df[qr][0] = lds_tr((const lds_u16*)(dsb + dso[qr][t][0]));
+                df[qr][1] = lds_tr((const lds_u16*)(dsb + dso[qr][t][1]));
+            }
+#pragma unroll
+            for (int qr = 0; qr < 2; ++qr)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[qr][db] = mfma32(as_bf16x8(u32x4_t{kf[db][0][0], kf[db][0][1], kf[db][1][0], kf[db][1][1]}),
+                                         as_bf16x8(u32x4_t{df[qr][0][0], df[qr][0][1], df[qr][1][0], df[qr][1][1]}),
+                                         acc[qr][db]);
+        }
+    }
+    // dQ^T accumulator of query block qr: lane = query row 32 qr + (l32 with bits 2 and 3
+    // swapped) of the tile, register r = d 32 db + 8 (r / 4) + 4 hh + r % 4
+    const int rloc = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+#pragma unroll
+    for (int qr = 0; qr < 2; ++qr) {
+        const int row = qt * 64 + 32 * qr + rloc;
+        if (row >= p.Sq) continue;
+        float* dqrow = p.dq + (int64_t)b * p.dq_sB + (int64_t)row * p.dq_sS + (int64_t)h * p.dq_sH;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4_t* pq = (f32x4_t*)(dqrow + 32 * db + 8 * g4 + 4 * hh);
+                f32x4_t v4 = *pq;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[j] += p.scale * acc[qr][db][4 * g4 + j];
+                *pq = v4;
+            }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
@@ -935,13 +1122,17 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
     p.v_bytes = span_bytes(v.S, v.sS, v.D);
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
+    p.km = nullptr;
+    p.km_sB = 0;
+    p.ds = nullptr;
+    p.ds_nqt = p.ds_nkg = 0;
     return p;
 }
 }  // namespace
 
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                                 const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
-                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s) {
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
     p.dk = (float*)dk_acc.data;
@@ -952,6 +1143,9 @@ hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra
     p.km_sB = km.sB;
     // one workgroup per (128-key tile, KV head)
     p.n_tiles = (k.S + kBwdBlockN - 1) / kBwdBlockN;
+    p.ds = (uint16_t*)ds;
+    p.ds_nqt = ds_query_tiles(q.S);
+    p.ds_nkg = ds_key_groups(k.S);
     const unsigned nb = (unsigned)p.n_tiles * k.H * q.B;
     if (q.D == 64) bwd_kv_bf16_kernel<64><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
     else bwd_kv_bf16_kernel<128><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
@@ -977,6 +1171,23 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
         if (q.D == 64) bwd_dq_bf16_kernel<64, false><<<nb, 256, 0, s>>>(p);
         else bwd_dq_bf16_kernel<128, false><<<nb, 256, 0, s>>>(p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
+                               const ra_tensor& dq_acc, hipStream_t s) {
+    if (q.S == 0 || k.S == 0) return hipSuccess;
+    BwdParams p = bwd_params(q, k, k, q, ra_lse{}, ra_lse{}, scale);
+    p.dq = (float*)dq_acc.data;
+    p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
+    p.ds = (uint16_t*)ds;
+    p.ds_nqt = ds_query_tiles(q.S);
+    p.ds_nkg = ds_key_groups(k.S);
+    // one workgroup per (kDqsWaves 64-row query tiles, query head)
+    p.n_tiles = (p.ds_nqt + kDqsWaves - 1) / kDqsWaves;
+    const unsigned nb = (unsigned)p.n_tiles * q.H * q.B;
+    if (q.D == 64) bwd_dqs_bf16_kernel<64><<<nb, 64 * kDqsWaves, 0, s>>>(p);
+    else bwd_dqs_bf16_kernel<128><<<nb, 64 * kDqsWaves, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -252,7 +252,7 @@ ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_ten
 ra_status enqueue_bwd_dkdv(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                            const ra_lse& lse, const ra_lse& delta, const ra::KeyMask& km, float scale,
                            const ra_tensor& dk, const ra_tensor& dv, hipStream_t s) {
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dkdv_bf16(q, k, v, dout, lse, delta, km, scale, dk, dv, s));
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_bwd_dkdv_bf16(q, k, v, dout, lse, delta, km, scale, dk, dv, nullptr, s));
     else RA_HIP(ra::launch_bwd_dkdv_f32(q, k, v, dout, lse, delta, km, scale, dk, dv, s));
     return RA_OK;
 }
@@ -401,6 +401,20 @@ size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
     return round256((size_t)numel(*q) * 4);
 }
 
+// dS region of the bf16 ring backward: enough for every query row against the whole key
+// sequence, capped at kDsBudget; a chunk whose dS does not fit is swept in query-row
+// slices (multiples of 64 rows) that do.
+static constexpr int64_t kDsBudget = int64_t(2) << 30;
+// a sliced chunk keeps the stored-dS route only while each slice's dQ pass has at least
+// this many workgroups (one per compute unit)
+static constexpr int64_t kMinSliceWorkgroups = 256;
+
+static size_t ds_region_bytes(const ra_tensor& q, const ra_tensor& k) {
+    if (q.dtype != RA_BF16 || q.S == 0 || k.S == 0) return 0;
+    const int64_t full = ra::ds_bytes(q.B, q.H, q.S, k.S);
+    return round256((size_t)(full < kDsBudget ? full : kDsBudget));
+}
+
 size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq, const ra_tensor* dk,
                                    const ra_tensor* dv) {
     if (!q || !k) return 0;
@@ -408,7 +422,15 @@ size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const
     if (dq && dq->dtype == RA_BF16) n += round256((size_t)numel(*q) * 4);
     if (dk && dk->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
     if (dv && dv->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
+    n += ds_region_bytes(*q, *k);
     return n;
+}
+
+static ra_lse rows_slice(const ra_lse& t, int32_t start, int32_t len) {
+    ra_lse r = t;
+    r.data = t.data + start;
+    r.S = len;
+    return r;
 }
 
 static ra_status check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -477,6 +499,8 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     if (dq->dtype == RA_BF16) { dq_acc = contiguous_f32(p, *q); p += round256((size_t)numel(*q) * 4); }
     if (dk->dtype == RA_BF16) { dk_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
     if (dv->dtype == RA_BF16) { dv_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
+    void* const ds = p;
+    const int64_t ds_room = (int64_t)ds_region_bytes(*q, *k);
 
     RA_HIP(ra::launch_bwd_delta(*out, *dout, delta, s));
     RA_HIP(ra::launch_zero_f32(dq_acc, s));
@@ -489,8 +513,25 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
         const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
         const ra_tensor dkc = seq_slice(dk_acc, chunks->start[c], chunks->len[c]);
         const ra_tensor dvc = seq_slice(dv_acc, chunks->start[c], chunks->len[c]);
-        RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, key_mask(kmask, chunks->start[c]), scale, dq_acc,
-                                 dkc, dvc, s));
+        const ra::KeyMask km = key_mask(kmask, chunks->start[c]);
+        // bf16: the dK/dV kernel stores dS, the dQ pass reads it back (no second S, dP);
+        // query rows go in slices whose dS fits the region
+        const int64_t per_tile = q->dtype == RA_BF16 ? ra::ds_bytes(q->B, q->H, 64, kc.S) : 0;
+        const int32_t rows = per_tile == 0 || per_tile > ds_room
+                                 ? 0
+                                 : (int32_t)std::min<int64_t>(64 * (ds_room / per_tile), (int64_t)q->S);
+        // slices so thin that the dQ pass cannot fill the chip: recompute instead
+        if (rows == 0 || (rows < q->S && ra::dqs_workgroups(q->B, q->H, rows) < kMinSliceWorkgroups)) {
+            RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, km, scale, dq_acc, dkc, dvc, s));
+            continue;
+        }
+        for (int32_t r0 = 0; r0 < q->S; r0 += rows) {
+            const int32_t n = std::min(rows, q->S - r0);
+            const ra_tensor qs = seq_slice(*q, r0, n), dos = seq_slice(*dout, r0, n), dqs = seq_slice(dq_acc, r0, n);
+            const ra_lse ls = rows_slice(*lse, r0, n), dls = rows_slice(delta, r0, n);
+            RA_HIP(ra::launch_bwd_dkdv_bf16(qs, kc, vc, dos, ls, dls, km, scale, dkc, dvc, ds, s));
+            RA_HIP(ra::launch_bwd_dqs_bf16(qs, kc, ds, scale, dqs, s));
+        }
     }
     if (dq->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));
     if (dk->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dk_acc, *dk, s));

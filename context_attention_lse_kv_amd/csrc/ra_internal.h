@@ -19,6 +19,20 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdBlockN = kBwdKeysPerWave * kBwdWaves;  // keys per workgroup
 constexpr int kBwdBlockM = 64;                            // query rows per LDS tile
 
+// dS workspace of the bf16 backward (written by the dK/dV kernel, read by the dQ pass):
+// one 4 KiB block (64 query rows x 32 keys, bf16) per (batch, query head, 32-key group,
+// 64-row query tile); key groups are counted up to whole 128-key workgroup tiles.
+constexpr int64_t kDsBlockBytes = 4096;
+inline int ds_query_tiles(int Sq) { return (Sq + 63) / 64; }
+inline int ds_key_groups(int Sk) { return 4 * ((Sk + kBwdBlockN - 1) / kBwdBlockN); }
+inline int64_t ds_bytes(int B, int Hq, int Sq, int Sk) {
+    return (int64_t)B * Hq * ds_query_tiles(Sq) * ds_key_groups(Sk) * kDsBlockBytes;
+}
+// the dQ pass over stored dS: kDqsWaves wavefronts, one 64-row query tile each, per workgroup
+constexpr int kDqsWaves = 8;
+inline int64_t dqs_workgroups(int B, int Hq, int Sq) {
+    return (int64_t)B * Hq * ((ds_query_tiles(Sq) + kDqsWaves - 1) / kDqsWaves);
+}
 constexpr int kMaxRanks = 16;  // exchange fan-out limit (kernel argument table)
 
 // Key mask of one chunk as the kernels see it: data[b * sB + key] != 0 means the key
@@ -44,9 +58,15 @@ hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra
                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
 // Backward chunk step, split: add this chunk's contribution to dk_acc/dv_acc, or to
 // dq_acc (all fp32).
+// ds: dS workspace of ds_bytes(q.B, q.H, q.S, k.S) bytes that receives this chunk
+// step's dS (bf16, zero for keys outside the chunk or masked), or null.
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                                 const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
-                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, hipStream_t s);
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s);
+// dq_acc += scale dS K from the dS workspace written by launch_bwd_dkdv_bf16 for the same
+// q rows and chunk k.
+hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
+                               const ra_tensor& dq_acc, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                               const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
                               const ra_tensor& dq_acc, hipStream_t s);

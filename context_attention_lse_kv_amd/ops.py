@@ -227,6 +227,17 @@ def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layou
     return dq, dk, dv
 
 
+def ring_bwd_workspace_bytes(q, k, dq_dtype=None, dk_dtype=None, layout="bshd"):
+    """Workspace bytes ``ring_bwd`` needs for these q, k (gradients of dtype
+    ``dq_dtype`` / ``dk_dtype``, default q's dtype): delta, fp32 accumulators for bf16
+    gradients and, on the bf16 path, the dS region."""
+    tq, tk = tensor_desc(q, layout), tensor_desc(k, layout)
+    tdq, tdk = tensor_desc(q, layout), tensor_desc(k, layout)
+    tdq.dtype = _DT[dq_dtype or q.dtype]
+    tdk.dtype = _DT[dk_dtype or k.dtype]
+    return lib().ra_ring_bwd_workspace_bytes(tq, tk, tdq, tdk, tdk)
+
+
 def _workspace(ws, need, device):
     if need == 0:
         return None

@@ -200,11 +200,17 @@ ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
                       const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse,
                       void* ws, size_t ws_bytes, void* stream);
 
-/* Backward sweep: delta from (out, dout), then one ra_bwd_chunk per step in
+/* Backward sweep: delta from (out, dout), then one chunk step per chunk in
  * the same order as the forward, each against its own chunk; dq, dk, dv
  * (bf16 or fp32, shapes of q, k, v) are written.  ws: at least
- * ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv) bytes (delta, and fp32
- * accumulators for any bf16 gradient). */
+ * ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv) bytes (delta, fp32
+ * accumulators for any bf16 gradient and, for bf16 inputs, a dS region of at
+ * most 2 GiB).  With bf16 inputs a chunk step computes the same quantities as
+ * ra_bwd_chunk by another route: the dK/dV kernel stores dS = P (dP - delta)
+ * in bf16 to the dS region and a second kernel forms dQ += scale dS K from it,
+ * instead of recomputing S and dP (query rows go in slices when the dS of a
+ * whole chunk does not fit the region).  Results agree with ra_bwd_chunk up to
+ * rounding, not bit for bit. */
 ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
                       const ra_tensor* out, const ra_tensor* dout, const ra_lse* lse,
                       const ra_chunks* chunks, float scale,

@@ -126,7 +126,8 @@ def test_all_ones_mask_equals_no_mask(dt):
 
 
 def test_masked_chunk_entry_points_match_ring():
-    """fwd_chunk/bwd_chunk(_dkdv/_dq) with the chunk's mask slice reproduce the masked ring."""
+    """fwd_chunk/bwd_chunk(_dkdv/_dq) with the chunk's mask slice reproduce the masked ring
+    (bit for bit except dQ, which the two reach by different routes)."""
     B, S, Sq, Hq, Hkv, D = 2, 400, 160, 4, 2, 128
     q, k, v, do = (W.randn(s, 980 + i, "bf16") for i, s in enumerate([(B, Sq, Hq, D), (B, S, Hkv, D),
                                                                       (B, S, Hkv, D), (B, Sq, Hq, D)]))
@@ -156,8 +157,12 @@ def test_masked_chunk_entry_points_match_ring():
             ra.bwd_chunk_dkdv(gq, gk[:, sl], gv[:, sl], gdo, lse, delta, dk[:, sl], dv[:, sl], 1, kmask=gm[:, sl])
             ra.bwd_chunk_dq(gq, gk[:, sl], gv[:, sl], gdo, lse, delta, dq, kmask=gm[:, sl])
     torch.cuda.synchronize()
-    for a, b in ((dq, dq_r), (dk, dk_r), (dv, dv_r)):
+    # dK/dV come from the same kernel in both; the ring forms dQ from the dS that kernel
+    # stored (fp16 P), the chunk entry point recomputes it (fp32 P): equal up to rounding
+    for a, b in ((dk, dk_r), (dv, dv_r)):
         assert torch.equal(a.to(torch.bfloat16), b)
+    rel = ((dq.to(torch.bfloat16).float() - dq_r.float()).norm() / dq_r.float().norm()).item()
+    assert rel < 5e-3, rel
 
 
 def test_masked_video_shard():

@@ -11,7 +11,8 @@ Prints ONE JSON line.  ``value`` is fwd+bwd TFLOP/s with the attention flop
 count 4*B*Hq*Sq*Sk*D (forward) + 10*B*Hq*Sq*Sk*D (backward, five products
 including the recompute).  ``roofline`` describes the dominant kernel (the
 dK/dV kernel of the backward chunk step), timed per launch with HIP events on
-the stream it runs on, each launch placed as in a ring step; ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
+the stream it runs on, each launch placed as in the backward sweep;
+``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
 import argparse
@@ -93,18 +94,18 @@ def run_workload(full, steps, warmup, masked=False, single=False):
 
 
 def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
-    """The dK/dV half of the backward chunk step (one kernel launch per call with
-    accumulate=1, which skips the zero fill).  It executes S = Q K^T, dP = dO V^T,
-    dV = P^T dO and dK = dS^T Q: 8*D flop per (query row, key) pair per head.
+    """The dK/dV half of the backward chunk step as the ring backward runs it (one
+    kernel launch per call with accumulate=1, which skips the zero fill; it also stores
+    the step's dS for the dQ pass).  It executes S = Q K^T, dP = dO V^T, dV = P^T dO and
+    dK = dS^T Q: 8*D flop per (query row, key) pair per head.
 
-    Each timed launch runs where it runs in a ring step: after the chunk's forward
-    kernel and its dQ kernel on the same stream, with a HIP event pair around the
-    dK/dV launch alone; the result is the mean of the per-launch event intervals.
-    The board's clock settles only under sustained load (after an idle gap it
-    boosts, overshoots its power limit and throttles for a few milliseconds), so
-    `lead_steps` whole ring steps are queued right before the timed launches, with
-    no host synchronisation in between.  `back_to_back=True` times `launches`
-    dK/dV launches in a row instead."""
+    Each timed launch runs where it runs in the backward sweep: after the previous
+    chunk's dQ pass on the same stream, with a HIP event pair around the dK/dV launch
+    alone; the result is the mean of the per-launch event intervals.  The board's clock
+    settles only under sustained load (after an idle gap it boosts, overshoots its power
+    limit and throttles for a few milliseconds), so `lead_steps` whole ring steps are
+    queued right before the timed launches, with no host synchronisation in between.
+    `back_to_back=True` times `launches` dK/dV launches in a row instead."""
     q, k, v, do, out, lse = r["q"], r["k"], r["v"], r["do"], r["out"], r["lse"]
     c = r["lens"][0]
     kc, vc = k[:, :c], v[:, :c]
@@ -112,8 +113,8 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
     ra.bwd_delta(out, do, delta)
     dk = torch.zeros(kc.shape, dtype=torch.float32, device=q.device)
     dv = torch.zeros_like(dk)
-    o2, l2 = torch.empty(out.shape, dtype=torch.float32, device=q.device), torch.empty_like(lse)
     dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    ds = torch.empty(ra.bwd_ds_bytes(q, kc), dtype=torch.uint8, device=q.device)
     w = r["w"]
     f = 8.0 * w.B * w.Hq * q.shape[1] * c * w.D
     s = torch.cuda.current_stream()
@@ -123,10 +124,9 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
         r["step"]()
     for i in range(launches):
         if not back_to_back:
-            ra.fwd_chunk(q, kc, vc, o2, l2, merge=i > 0)
-            ra.bwd_chunk_dq(q, kc, vc, do, lse, delta, dq)
+            ra.bwd_chunk_dq_ds(q, kc, ds, dq)
         ev[i][0].record(s)
-        ra.bwd_chunk_dkdv(q, kc, vc, do, lse, delta, dk, dv, accumulate=1)
+        ra.bwd_chunk_dkdv_ds(q, kc, vc, do, lse, delta, dk, dv, 1, ds)
         ev[i][1].record(s)
     torch.cuda.synchronize()
     t = sum(a.elapsed_time(b) for a, b in ev) / launches / 1e3
@@ -254,7 +254,7 @@ def main():
         "bwd_tflops": round(r["f_b"] / r["t_bwd"] / 1e12, 2),
         "fwd_ms": round(r["t_fwd"] * 1e3, 4),
         "bwd_ms": round(r["t_bwd"] * 1e3, 4),
-        "roofline": {"bound": "mfma", "kernel": "bwd_kv_bf16_kernel<128> (dK/dV of one ring step: 4096 q rows x 4096 keys x 32 heads)",
+        "roofline": {"bound": "mfma", "kernel": "bwd_kv_bf16_kernel<128> (dK/dV of one ring step, storing dS: 4096 q rows x 4096 keys x 32 heads)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(t_k * 1e3, 4),
                      "avg_launch_ms_back_to_back": round(t_b2b * 1e3, 4),

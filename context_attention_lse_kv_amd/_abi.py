@@ -21,6 +21,7 @@ EXPORTS = [
     "ra_ring_fwd", "ra_ring_bwd",
     "ra_fwd_chunk_masked", "ra_bwd_chunk_masked", "ra_bwd_chunk_dkdv_masked", "ra_bwd_chunk_dq_masked",
     "ra_ring_fwd_masked", "ra_ring_bwd_masked",
+    "ra_bwd_ds_bytes", "ra_bwd_chunk_dkdv_ds", "ra_bwd_chunk_dq_ds",
     "ra_ring_fwd_workspace_bytes", "ra_ring_bwd_workspace_bytes", "ra_seq_head_permute",
     "ra_split_sizes", "ra_ring_order", "ra_status_string", "ra_last_error", "ra_version",
 ]
@@ -68,6 +69,9 @@ _SIGS = {
     "ra_bwd_chunk_dq_masked": (i32, [T, T, T, T, L, L, K, f32, T, vp]),
     "ra_ring_fwd_masked": (i32, [T, T, T, K, C, f32, T, L, vp, sz, vp]),
     "ra_ring_bwd_masked": (i32, [T, T, T, T, T, L, K, C, f32, T, T, T, vp, sz, vp]),
+    "ra_bwd_ds_bytes": (sz, [T, T]),
+    "ra_bwd_chunk_dkdv_ds": (i32, [T, T, T, T, L, L, K, f32, T, T, i32, vp, sz, vp]),
+    "ra_bwd_chunk_dq_ds": (i32, [T, T, vp, sz, f32, T, vp]),
     "ra_ring_fwd_workspace_bytes": (sz, [T, T]),
     "ra_ring_bwd_workspace_bytes": (sz, [T, T, T, T, T]),
     "ra_seq_head_permute": (i32, [T, i32, T, i32, i32, vp]),

@@ -396,6 +396,61 @@ ra_status ra_bwd_chunk_dq(const ra_tensor* q, const ra_tensor* k, const ra_tenso
     return ra_bwd_chunk_dq_masked(q, k, v, dout, lse, delta, nullptr, scale, dq_acc, stream);
 }
 
+size_t ra_bwd_ds_bytes(const ra_tensor* q, const ra_tensor* k) {
+    if (!q || !k || q->dtype != RA_BF16 || q->S <= 0 || k->S <= 0) return 0;
+    return round256((size_t)ra::ds_bytes(q->B, q->H, q->S, k->S));
+}
+
+static ra_status check_ds(const ra_tensor& q, const ra_tensor& k, const void* ds, size_t ds_bytes) {
+    if (q.dtype != RA_BF16) return fail(RA_E_DTYPE, "the stored-dS route is bf16 only");
+    const size_t need = ra_bwd_ds_bytes(&q, &k);
+    if (need == 0) return RA_OK;
+    // the dQ pass addresses one (batch, head) slab of blocks with 32-bit buffer offsets
+    if (ra::ds_bytes(1, 1, q.S, k.S) > ((int64_t)1 << 31))
+        return fail(RA_E_UNSUPPORTED, "dS of one (batch, head) spans %lld bytes; the dQ pass needs <= 2^31",
+                    (long long)ra::ds_bytes(1, 1, q.S, k.S));
+    if (!ds) return fail(RA_E_WORKSPACE, "ds buffer of %zu bytes needed, got NULL", need);
+    if ((uintptr_t)ds % 256) return fail(RA_E_ALIGN, "ds buffer must be 256-byte aligned");
+    if (ds_bytes < need) return fail(RA_E_WORKSPACE, "ds buffer of %zu bytes needed, got %zu", need, ds_bytes);
+    return RA_OK;
+}
+
+ra_status ra_bwd_chunk_dkdv_ds(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_tensor* dout,
+                               const ra_lse* lse, const ra_lse* delta, const ra_kmask* kmask, float scale,
+                               ra_tensor* dk_acc, ra_tensor* dv_acc, int32_t accumulate, void* ds, size_t ds_bytes,
+                               void* stream) {
+    RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
+    RA_TRY(check_kmask(kmask, q->B, k->S));
+    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
+    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
+    if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
+    RA_TRY(check_ds(*q, *k, ds, ds_bytes));
+    hipStream_t s = (hipStream_t)stream;
+    if (!accumulate) {
+        RA_HIP(ra::launch_zero_f32(*dk_acc, s));
+        RA_HIP(ra::launch_zero_f32(*dv_acc, s));
+    }
+    if (k->S > 0 && q->S > 0)
+        RA_HIP(ra::launch_bwd_dkdv_bf16(*q, *k, *v, *dout, *lse, *delta, key_mask(kmask), scale, *dk_acc, *dv_acc,
+                                        ds, s));
+    return ok();
+}
+
+ra_status ra_bwd_chunk_dq_ds(const ra_tensor* q, const ra_tensor* k, const void* ds, size_t ds_bytes, float scale,
+                             ra_tensor* dq_acc, void* stream) {
+    RA_TRY(check_tensor(q, "q"));
+    RA_TRY(check_tensor(k, "k"));
+    if (q->B != k->B || q->D != k->D) return fail(RA_E_SHAPE, "q and k must agree in B and D");
+    if (k->H <= 0 || q->H % k->H) return fail(RA_E_SHAPE, "Number of heads in key/value must divide number of heads in query");
+    if (k->dtype != q->dtype) return fail(RA_E_DTYPE, "q and k must have the same dtype");
+    RA_TRY(check_scale(scale));
+    RA_TRY(check_span32(*k, "k"));
+    RA_TRY(check_acc(dq_acc, "dq_acc", *q));
+    RA_TRY(check_ds(*q, *k, ds, ds_bytes));
+    if (k->S > 0 && q->S > 0) RA_HIP(ra::launch_bwd_dqs_bf16(*q, *k, ds, scale, *dq_acc, (hipStream_t)stream));
+    return ok();
+}
+
 size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
     if (!q || !out || out->dtype != RA_BF16) return 0;
     return round256((size_t)numel(*q) * 4);

@@ -164,6 +164,34 @@ def bwd_chunk_dq(q, k, v, dout, lse, delta, dq_acc, scale=None, layout="bshd", k
                                            kmask_desc(kmask), sc, d[4], _stream(q)), "ra_bwd_chunk_dq_masked")
 
 
+def bwd_ds_bytes(q, k, layout="bshd"):
+    """Bytes of the dS buffer ``bwd_chunk_dkdv_ds`` writes for these q rows and chunk k."""
+    return lib().ra_bwd_ds_bytes(tensor_desc(q, layout), tensor_desc(k, layout))
+
+
+def bwd_chunk_dkdv_ds(q, k, v, dout, lse, delta, dk_acc, dv_acc, accumulate, ds, scale=None, layout="bshd",
+                      kmask=None):
+    """dK/dV half of the bf16 chunk step that also stores dS into ``ds`` (a device
+    buffer of at least ``bwd_ds_bytes(q, k)`` bytes) for ``bwd_chunk_dq_ds``."""
+    _dev_check(q, k, v, dout, lse, delta, dk_acc, dv_acc, ds)
+    d = [tensor_desc(x, layout) for x in (q, k, v, dout, dk_acc, dv_acc)]
+    nbytes = ds.numel() * ds.element_size()
+    m = kmask_desc(kmask) if kmask is not None else None
+    check(lib().ra_bwd_chunk_dkdv_ds(d[0], d[1], d[2], d[3], rows_desc(lse), rows_desc(delta), m,
+                                     _scale(scale, q.shape[-1]), d[4], d[5], int(accumulate),
+                                     ctypes.c_void_p(ds.data_ptr()), nbytes, _stream(q)), "ra_bwd_chunk_dkdv_ds")
+
+
+def bwd_chunk_dq_ds(q, k, ds, dq_acc, scale=None, layout="bshd"):
+    """dq_acc += scale dS K from the dS that ``bwd_chunk_dkdv_ds`` stored for the same
+    q rows and chunk k."""
+    _dev_check(q, k, ds, dq_acc)
+    dq_, dk_, dd = (tensor_desc(x, layout) for x in (q, k, dq_acc))
+    nbytes = ds.numel() * ds.element_size()
+    check(lib().ra_bwd_chunk_dq_ds(dq_, dk_, ctypes.c_void_p(ds.data_ptr()), nbytes, _scale(scale, q.shape[-1]),
+                                   dd, _stream(q)), "ra_bwd_chunk_dq_ds")
+
+
 def _rows_shape(q, layout):
     if layout == "bshd":
         B, S, H, _ = q.shape

@@ -188,6 +188,24 @@ ra_status ra_bwd_chunk_dq_masked(const ra_tensor* q, const ra_tensor* k, const r
                                  const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
                                  const ra_kmask* kmask, float scale, ra_tensor* dq_acc, void* stream);
 
+/* The bf16 chunk step by the stored-dS route (what ra_ring_bwd runs for bf16
+ * inputs): ra_bwd_chunk_dkdv_ds is ra_bwd_chunk_dkdv_masked that also writes
+ * the step's dS = P (dP - delta) (bf16; zero for masked keys) to the device
+ * buffer ds; ra_bwd_chunk_dq_ds then adds scale dS K to dq_acc (fp32) from that
+ * buffer, with the same q (rows), k (chunk) and scale, without forming S and dP
+ * again.  ds must hold ra_bwd_ds_bytes(q, k) bytes (256-byte aligned); its
+ * layout is private to these two calls.  bf16 only (RA_E_DTYPE otherwise);
+ * ds too small or NULL: RA_E_WORKSPACE.  The result equals ra_bwd_chunk's up
+ * to rounding (P reaches dS through fp16 here). */
+size_t ra_bwd_ds_bytes(const ra_tensor* q, const ra_tensor* k);
+ra_status ra_bwd_chunk_dkdv_ds(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                               const ra_tensor* dout, const ra_lse* lse, const ra_lse* delta,
+                               const ra_kmask* kmask, float scale, ra_tensor* dk_acc,
+                               ra_tensor* dv_acc, int32_t accumulate, void* ds, size_t ds_bytes,
+                               void* stream);
+ra_status ra_bwd_chunk_dq_ds(const ra_tensor* q, const ra_tensor* k, const void* ds,
+                             size_t ds_bytes, float scale, ra_tensor* dq_acc, void* stream);
+
 /* ---------------------------------------------------------------- ring sweeps */
 
 /* Forward sweep of the local query shard over every chunk in chunks->order:

@@ -179,6 +179,57 @@ def test_ring_bwd_workspace_sizes():
     assert full >= base + (100 * 8 * 64 + 2 * 300 * 2 * 64) * 4
 
 
+def test_bwd_ds_bytes_and_ring_ds_region():
+    """dS blocks: 4 KiB per (batch, query head, 64 query rows, 32 keys counted in whole
+    128-key tiles); the ring backward reserves min(2 GiB, that for the whole key sequence)
+    for bf16 inputs and nothing for fp32."""
+    lib = _lib()
+    q, k = T(2, 100, 8, 64), T(2, 300, 2, 64)
+    assert lib.ra_bwd_ds_bytes(q, k) == 2 * 8 * 2 * (4 * 3) * 4096
+    assert lib.ra_bwd_ds_bytes(T(1, 4096, 32, 128), T(1, 4096, 8, 128)) == 1 << 30
+    assert lib.ra_bwd_ds_bytes(T(2, 100, 8, 64, abi.RA_F32), T(2, 300, 2, 64, abi.RA_F32)) == 0
+    assert lib.ra_bwd_ds_bytes(T(2, 0, 8, 64), k) == 0
+    f = lambda t: T(t.B, t.S, t.H, t.D, abi.RA_F32)
+    with_ds = lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k))
+    q32, k32 = f(q), f(k)
+    without = lib.ra_ring_bwd_workspace_bytes(q32, k32, q32, k32, k32)
+    assert with_ds - without == lib.ra_bwd_ds_bytes(q, k)
+    big_q, big_k = T(1, 32768, 32, 128), T(1, 32768, 8, 128)
+    fq, fk = f(big_q), f(big_k)
+    assert lib.ra_ring_bwd_workspace_bytes(big_q, big_k, fq, fk, fk) - \
+        lib.ra_ring_bwd_workspace_bytes(fq, fk, fq, fk, fk) == 2 << 30
+
+
+def test_stored_ds_entry_points_refuse():
+    lib = _lib()
+    q, k, v = T(1, 64, 8, 64), T(1, 64, 2, 64), T(1, 64, 2, 64)
+    l = Lrows(1, 8, 64)
+    acc_k = T(1, 64, 2, 64, abi.RA_F32)
+    acc_q = T(1, 64, 8, 64, abi.RA_F32)
+    need = lib.ra_bwd_ds_bytes(q, k)
+
+    def kv(ds, nbytes, **kw):
+        a = dict(q=q, k=k, v=v, acc=acc_k, acc_v=acc_k, accumulate=1)
+        a.update(kw)
+        st = lib.ra_bwd_chunk_dkdv_ds(a["q"], a["k"], a["v"], a["q"], l, l, None, 0.125, a["acc"], a["acc_v"],
+                                      a["accumulate"], ds, nbytes, None)
+        return st
+
+    assert kv(None, 0) == abi.RA_E_WORKSPACE
+    assert kv(FAKE, need - 1) == abi.RA_E_WORKSPACE
+    assert kv(FAKE + 16, need) == abi.RA_E_ALIGN
+    assert kv(FAKE, need, accumulate=2) == abi.RA_E_ARG
+    assert kv(FAKE, need, acc=T(1, 64, 2, 64)) == abi.RA_E_DTYPE
+    q32, k32 = T(1, 64, 8, 64, abi.RA_F32), T(1, 64, 2, 64, abi.RA_F32)
+    assert kv(FAKE, need, q=q32, k=k32, v=k32) == abi.RA_E_DTYPE
+    assert lib.ra_bwd_chunk_dq_ds(q, k, None, 0, 0.125, acc_q, None) == abi.RA_E_WORKSPACE
+    assert lib.ra_bwd_chunk_dq_ds(q, k, FAKE, need - 256, 0.125, acc_q, None) == abi.RA_E_WORKSPACE
+    assert lib.ra_bwd_chunk_dq_ds(q, T(1, 64, 3, 64), FAKE, need, 0.125, acc_q, None) == abi.RA_E_SHAPE
+    assert lib.ra_bwd_chunk_dq_ds(q, k, FAKE, need, -1.0, acc_q, None) == abi.RA_E_ARG
+    assert lib.ra_bwd_chunk_dq_ds(q, k, FAKE, need, 0.125, T(1, 64, 8, 64), None) == abi.RA_E_DTYPE
+    assert lib.ra_bwd_chunk_dq_ds(q32, k32, FAKE, need, 0.125, acc_q, None) == abi.RA_E_DTYPE
+
+
 def test_bwd_chunk_refuses_bf16_accumulators():
     lib = _lib()
     q, k, v = T(1, 64, 8, 64), T(1, 64, 2, 64), T(1, 64, 2, 64)

@@ -22,11 +22,13 @@
 // query rows of every query head of that GQA group in LDS tiles of 64; each 32-key
 // group has two wavefronts in split roles (S, P, dV and dP, dS, dK) running one Q
 // tile apart, and the workgroup adds its dK/dV rows with plain read-modify-writes.
-// The Q-stationary kernel owns 128 query rows like the forward, recomputes S^T and
-// dP^T per key tile and accumulates dQ^T += K^T dS^T in registers, so each row's dQ
-// has a single writer.  The recompute of S and dP in both kernels (7 products
-// instead of 5) is cheaper on this chip than adding dQ through device-scope atomics
-// from every key tile.
+// dQ takes one of two routes, both free of atomics (adding dQ from every key tile
+// through device-scope atomics costs more on this chip than either).  Stored dS: the
+// KV-stationary kernel also writes the dS it holds (bf16) to a caller buffer, and a
+// streaming kernel forms dQ^T += K^T dS^T from it (5 products in all, 4 bytes per
+// (row, key) through HBM).  Recompute: a Q-stationary kernel owns 128 query rows like
+// the forward, recomputes S^T and dP^T per key tile and accumulates dQ^T += K^T dS^T in
+// registers (7 products, no buffer).  Either way each row's dQ has a single writer.
 //
 // All kernels stream their tiles HBM -> LDS with buffer->LDS copies (rows past the
 // end of a slice arrive as zeros, so tails need no branches), into unpadded rows with

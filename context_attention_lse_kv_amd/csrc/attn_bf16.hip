@@ -35,6 +35,8 @@
 // an XOR swizzle of 16-byte chunks, one tile ahead of use, with one barrier per tile;
 // the per-tile work is unrolled into slots closed by scheduling barriers so that the
 // operand reads stay ahead of the MFMAs that consume them.
+#include <type_traits>
+
 #include "ra_device.h"
 
 #define RA_LDS __attribute__((address_space(3)))
@@ -280,8 +282,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     constexpr int NSS = 2 * KS, NSLOT = NSS + 4 * DB;
     constexpr int PF = 4, LT = 2;
     const int ntiles = (p.Sk + BN - 1) / BN;
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1, n0 = it * BN;
+    // the loop body per buffer parity, so that the LDS addresses fold into immediates
+    auto tile = [&](const int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        const int n0 = it * BN;
         const bool more = it + 1 < ntiles;
         const bool last = n0 + BN > p.Sk;
         const uint64_t kl = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) >> (4 * hh) : 0;  // this tile's key bits
@@ -385,6 +389,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         }
         if (more) wait_vmem();
         __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+        tile(it, std::integral_constant<int, 0>{});
+        if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
     }
 
     l = half_sum(l);
@@ -552,19 +560,21 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16_t{};
     // lane-constant LDS offsets: row reads (S, dP operands) and transposing reads (dV, dK)
+    // (the role's tile within a Q/dO buffer pair is folded into these: S reads Q rows and
+    // dP reads dO rows; dV reads dO^T and dK reads Q^T)
+    const int own_off = role == 0 ? 0 : TILEB;
+    const int oth_off = role == 0 ? TILEB : 0;
     const int sw_row = swz<RC>(l32);
     int ra_off[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ra_off[ks] = l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
+    for (int ks = 0; ks < KS; ++ks) ra_off[ks] = own_off + l32 * ROWB + 16 * ((2 * ks + hh) ^ sw_row);
     const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
     int tr_off[DB], tr_off8[DB];  // transposing reads of rows r and r + 8
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
-        tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
+        tr_off[db] = oth_off + (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
+        tr_off8[db] = oth_off + (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
     }
-    const int own_off = role == 0 ? 0 : TILEB;    // S: Q rows, dP: dO rows
-    const int oth_off = role == 0 ? TILEB : 0;    // dV: dO^T, dK: Q^T
 
     // Iteration slots (two MFMAs each): slot s runs the S/dP MFMA of row block s / KS at
     // k-step s % KS (tile t) and the dV/dK MFMA of group grp, column block db, j = s
@@ -584,12 +594,14 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     commit_stats(0);
     if (ntiles > 1) issue(1);
     __syncthreads();
-    int cur = 0;  // buffer of tile t; tile t-1 sits in (cur + 2) % 3
     int ds_h = g * p.G, ds_t = 0;  // query head and 64-row tile of tile t-1 (dS store)
-    for (int it = 0; it <= ntiles; ++it) {
-        const int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
-        const RA_LDS char* rowb = lbase + 2 * cur * TILEB + own_off;
-        const RA_LDS char* trb = lbase + 2 * prv * TILEB + oth_off;
+    // iteration it uses buffer cur = it % 3 for tile t = it (tile t-1 sits in (cur + 2) % 3);
+    // the body is instantiated per cur so that the LDS addresses fold into immediates
+    auto iteration = [&](const int it, auto curc) {
+        constexpr int cur = decltype(curc)::value;
+        constexpr int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
+        const RA_LDS char* rowb = lbase + 2 * cur * TILEB;
+        const RA_LDS char* trb = lbase + 2 * prv * TILEB;
         RA_LDS u32x4_t* const pw = pbuf + ((it & 1) * kBwdWaves + kg) * (2 * RB) * 64 + lane;        // P of tile t
         const RA_LDS u32x4_t* const pr = pbuf + (((it + 1) & 1) * kBwdWaves + kg) * (2 * RB) * 64 + lane;  // P of tile t-1
 
@@ -622,14 +634,23 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                 char* blk = (char*)p.ds +
                             ((((int64_t)b * p.Hq + ds_h) * p.ds_nkg + n0 / 32 + kg) * p.ds_nqt + ds_t) * 4096 +
                             l32 * 32 + hh * 16;
+                if (ds_zap) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                    for (int t2 = 0; t2 < 2; ++t2) {
-                        u32x4_t v = pk[rb][t2];
-                        if (ds_zap) v = u32x4_t{v[0] & ds_keep, v[1] & ds_keep, v[2] & ds_keep, v[3] & ds_keep};
-                        __builtin_nontemporal_store(v, (u32x4_t*)(blk + (2 * rb + t2) * 1024));
-                    }
+                        for (int t2 = 0; t2 < 2; ++t2) {
+                            const u32x4_t v = pk[rb][t2];
+                            __builtin_nontemporal_store(
+                                u32x4_t{v[0] & ds_keep, v[1] & ds_keep, v[2] & ds_keep, v[3] & ds_keep},
+                                (u32x4_t*)(blk + (2 * rb + t2) * 1024));
+                        }
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int t2 = 0; t2 < 2; ++t2)
+                            __builtin_nontemporal_store(pk[rb][t2], (u32x4_t*)(blk + (2 * rb + t2) * 1024));
+                }
                 if (++ds_t == ntq) {
                     ds_t = 0;
                     ++ds_h;
@@ -697,7 +718,11 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         }
         __syncthreads();
         if (it + 2 < ntiles) issue(prv);  // tile it + 2
-        cur = nxt;
+    };
+    for (int it = 0; it <= ntiles; it += 3) {
+        iteration(it, std::integral_constant<int, 0>{});
+        if (it + 1 <= ntiles) iteration(it + 1, std::integral_constant<int, 1>{});
+        if (it + 2 <= ntiles) iteration(it + 2, std::integral_constant<int, 2>{});
     }
 
     // dV (role 0) or dK (role 1) rows of this group's 32 keys: lane = d column,

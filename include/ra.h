@@ -189,7 +189,9 @@ ra_status ra_bwd_chunk_dq_masked(const ra_tensor* q, const ra_tensor* k, const r
                                  const ra_kmask* kmask, float scale, ra_tensor* dq_acc, void* stream);
 
 /* The bf16 chunk step by the stored-dS route (what ra_ring_bwd runs for bf16
- * inputs): ra_bwd_chunk_dkdv_ds is ra_bwd_chunk_dkdv_masked that also writes
+ * inputs; the same step as ra_bwd_chunk, [P1] "Root cause" and "Expected
+ * behavior": each backward step against its own chunk, dQ local, dK/dV of the
+ * chunk): ra_bwd_chunk_dkdv_ds is ra_bwd_chunk_dkdv_masked that also writes
  * the step's dS = P (dP - delta) (bf16; zero for masked keys) to the device
  * buffer ds; ra_bwd_chunk_dq_ds then adds scale dS K to dq_acc (fp32) from that
  * buffer, with the same q (rows), k (chunk) and scale, without forming S and dP

@@ -133,6 +133,46 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
     return t, f
 
 
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def hbm_kernels(r, reps=10):
+    """The HBM-bound kernels of the path at the video shard's sizes, timed with HIP events
+    on the current stream: the in-device Ulysses exchange of the whole 32k sequence over 8
+    simulated ranks (seq -> head, the 4096-row query shard as every rank's input), the
+    standalone LSE merge of two fp32 partials and the backward's delta.  Bytes are the
+    algorithmic reads + writes of one launch."""
+    q, out, do, lse = r["q"], r["out"], r["do"], r["lse"]
+    B, Sq, Hq, D = q.shape
+    R = 8
+    parts = [torch.empty((B, Sq * R, Hq // R, D), dtype=q.dtype, device=q.device) for _ in range(R)]
+    o_acc = torch.randn(q.shape, dtype=torch.float32, device=q.device)
+    o_part = torch.randn(q.shape, dtype=torch.float32, device=q.device)
+    l_acc, l_part = torch.randn_like(lse), torch.randn_like(lse)
+    delta = torch.empty_like(lse)
+    cases = {
+        "ulysses_exchange_8_ranks": (lambda: ra.seq_head_permute([q] * R, parts, 0, "bshd"), 2 * R * q.numel() * 2),
+        "merge_lse": (lambda: ra.merge_lse(o_acc, l_acc, o_part, l_part), 3 * o_acc.numel() * 4 + 3 * lse.numel() * 4),
+        "bwd_delta": (lambda: ra.bwd_delta(out, do, delta), 2 * out.numel() * 2 + lse.numel() * 4),
+    }
+    res = {}
+    s = torch.cuda.current_stream()
+    for name, (fn, nbytes) in cases.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(reps):
+            fn()
+        b.record(s)
+        b.synchronize()
+        t = a.elapsed_time(b) / reps / 1e3
+        gbps = nbytes / t / 1e9
+        res[name] = {"ms": round(t * 1e3, 4), "bytes": int(nbytes), "GB/s": round(gbps, 1),
+                     "frac": round(gbps / HBM_PEAK_GBPS, 3)}
+    return res
+
+
 KERNEL_SRC = os.path.join(ROOT, "context_attention_lse_kv_amd", "csrc", "attn_bf16.hip")
 PROFILE = os.path.join(ROOT, "profiles", "bwd_kv_bf16_video_dit_shard.md")
 
@@ -260,6 +300,7 @@ def main():
                      "avg_launch_ms_back_to_back": round(t_b2b * 1e3, 4),
                      "traffic": measured_traffic()},
     }
+    res["hbm_kernels"] = hbm_kernels(r)
     del r
     torch.cuda.empty_cache()
     if not args.no_full:

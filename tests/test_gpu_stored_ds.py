@@ -24,6 +24,8 @@ CASES = [
     ("d64_b2", 2, 512, 200, 4, 4, 64, (256, 256), (0, 1), None),
     ("d128_gqa_masked", 2, 640, 256, 4, 2, 128, (300, 340), (0, 1),
      dict(p_keep=0.8, valid_len=(640, 450), masked_ranges=[(0, 0, 100)])),
+    ("d128_ragged_rows_and_keys", 1, 700, 200, 8, 2, 128, (350, 350), (1, 0), None),
+    ("tiny_17_rows_37_keys", 1, 37, 17, 4, 1, 128, (20, 17), (0, 1), None),
 ]
 
 
@@ -101,7 +103,7 @@ def test_stored_ds_route_agrees_with_recompute_route(case):
 def test_stored_ds_masked_keys_store_zero_and_values_never_read():
     """Masked keys contribute nothing to dQ: changing K and V at masked keys leaves every
     gradient of the unmasked keys and dQ unchanged."""
-    case = CASES[2]
+    case = next(c for c in CASES if c[0] == "d128_gqa_masked")
     name, B, S, Sq, Hq, Hkv, D, lens, order, recipe = case
     q, k, v, do, m = _inputs(case)
     d = dev()

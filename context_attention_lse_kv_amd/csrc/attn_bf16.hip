@@ -934,16 +934,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
 // dQ = scale dS K with the dS blocks the dK/dV kernel wrote, so S and dP are not formed a
 // second time.  Workgroup = kDqsWaves wavefronts x one 64-row query tile each, of one query
 // head; sweeps the chunk's keys in tiles of 32 (one dS block per wavefront and tile; the
-// workgroup's blocks of a tile are adjacent in memory)
-// through a ring of kDqsStages LDS stages, so that three tiles are in flight while one is
-// used: the kernel is bound by reading dS from HBM.  dQ^T += K^T dS^T takes both operands
-// with transposing reads (K^T like V^T in the forward; dS^T from the key-major blocks).
-// The operands' shared k index runs over the 16 keys of a step in the order 4 hh + (0..3),
-// 8 + 4 hh + (0..3) for lane half hh, as in the forward.
-//   A dS block's 16-byte chunk c = 64 grp + 2 key + hh holds dS[key][8 hh .. 8 hh + 7] of
-// the 16-row group grp in the lane order of the dK/dV kernel's A operand: entry 8 hh + i
-// is query row 16 grp + 4 hh + (i & 3) + 8 (i >> 2), i.e. bits 2 and 3 of the row index
-// swapped.  In LDS the four-key quads of odd groups are swapped pairwise (chunk
+// workgroup's blocks of a tile are adjacent in memory) through a ring of kDqsStages LDS
+// stages, so that three tiles are in flight while one is used: the kernel is bound by
+// reading dS from HBM.  dQ^T += K^T dS^T takes both operands with transposing reads (K^T
+// like V^T in the forward; dS^T from the key-major blocks).  The operands' shared k index
+// runs over the 16 keys of a step in the order 4 hh + (0..3), 8 + 4 hh + (0..3) for lane
+// half hh, as in the forward.
+//   A dS block's 16-byte chunk c = 64 grp + 2 key + hh holds 8 entries of one key (row
+// of the block) and the 16-row query group grp, in the lane order of the dK/dV kernel's
+// A operand: entry 8 hh + i is dS at query row 16 grp + 4 hh + (i & 3) + 8 (i >> 2) of the
+// 64-row tile (the row index with bits 2 and 3 swapped).  In LDS the four-key quads of odd groups are swapped pairwise (chunk
 // c ^ 8 (grp & 1)) so that the four 16-lane quarters of a transposing read cover both
 // halves of the banks.
 constexpr int kDqsStages = 4;

@@ -38,15 +38,30 @@ def flops(B, Hq, Sq, Sk, D):
     return 4.0 * B * Hq * Sq * Sk * D, 10.0 * B * Hq * Sq * Sk * D
 
 
-def timed(fn, steps, warmup):
+def timed(fn, steps, warmup, per_step=None):
+    """Mean seconds per call over `steps` calls between two synchronisations.  With
+    `per_step` (a list), a HIP event pair around each call on the current stream also
+    records every call's duration in ms (events do not synchronise the timed region)."""
     for _ in range(warmup):
         fn()
+    ev = []
+    s = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
+        if per_step is not None:
+            a = torch.cuda.Event(enable_timing=True)
+            a.record(s)
         fn()
+        if per_step is not None:
+            b = torch.cuda.Event(enable_timing=True)
+            b.record(s)
+            ev.append((a, b))
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    t = (time.perf_counter() - t0) / steps
+    if per_step is not None:
+        per_step.extend(a.elapsed_time(b) for a, b in ev)
+    return t
 
 
 def setup(Sq_rows, full):
@@ -85,12 +100,13 @@ def run_workload(full, steps, warmup, masked=False, single=False):
         fwd()
         bwd()
 
-    t_step = timed(step, steps, warmup)
+    step_ms = []
+    t_step = timed(step, steps, warmup, step_ms)
     t_fwd = timed(fwd, max(3, steps // 2), 1)
     t_bwd = timed(bwd, max(3, steps // 2), 1)
     f_f, f_b = flops(w.B, w.Hq, q.shape[1], w.S, w.D)
     return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, t_step=t_step, t_fwd=t_fwd,
-                t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step)
+                t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step, step_ms=step_ms)
 
 
 def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
@@ -224,7 +240,14 @@ def cpu_baseline(target_s=10.0):
         spent += time.perf_counter() - t0
         heads += 1
     fl = 14.0 * heads * q.shape[1] * w.S * w.D
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host": {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": threads},
             "sample": f"oracle fwd+bwd (numpy fp64) of query heads 0..{heads - 1} of the rank-0 shard "
                       f"({q.shape[1]} rows each, all {w.S} keys of the head's kv head); {spent:.1f} s wall; "
                       f"same 14*Sq*Sk*D flop count"}
@@ -292,6 +315,8 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(r["f_f"] / r["t_fwd"] / 1e12, 2),
         "bwd_tflops": round(r["f_b"] / r["t_bwd"] / 1e12, 2),
+        "step_ms_events": {"median": round(sorted(r["step_ms"])[len(r["step_ms"]) // 2], 4),
+                           "min": round(min(r["step_ms"]), 4), "max": round(max(r["step_ms"]), 4)},
         "fwd_ms": round(r["t_fwd"] * 1e3, 4),
         "bwd_ms": round(r["t_bwd"] * 1e3, 4),
         "roofline": {"bound": "mfma", "kernel": "bwd_kv_bf16_kernel<128> (dK/dV of one ring step, storing dS: 4096 q rows x 4096 keys x 32 heads)",

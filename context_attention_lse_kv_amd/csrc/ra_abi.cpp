@@ -459,7 +459,7 @@ size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
 // dS region of the bf16 ring backward: enough for every query row against the whole key
 // sequence, capped at kDsBudget; a chunk whose dS does not fit is swept in query-row
 // slices (multiples of 64 rows) that do.
-static constexpr int64_t kDsBudget = int64_t(2) << 30;
+static constexpr int64_t kDsBudget = int64_t(8) << 30;
 // a sliced chunk keeps the stored-dS route only while each slice's dQ pass has at least
 // this many workgroups (one per compute unit)
 static constexpr int64_t kMinSliceWorkgroups = 256;

@@ -225,7 +225,7 @@ ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
  * (bf16 or fp32, shapes of q, k, v) are written.  ws: at least
  * ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv) bytes (delta, fp32
  * accumulators for any bf16 gradient and, for bf16 inputs, a dS region of at
- * most 2 GiB).  With bf16 inputs a chunk step computes the same quantities as
+ * most 8 GiB).  With bf16 inputs a chunk step computes the same quantities as
  * ra_bwd_chunk by another route: the dK/dV kernel stores dS = P (dP - delta)
  * in bf16 to the dS region and a second kernel forms dQ += scale dS K from it,
  * instead of recomputing S and dP (query rows go in slices when the dS of a

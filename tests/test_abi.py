@@ -181,7 +181,7 @@ def test_ring_bwd_workspace_sizes():
 
 def test_bwd_ds_bytes_and_ring_ds_region():
     """dS blocks: 4 KiB per (batch, query head, 64 query rows, 32 keys counted in whole
-    128-key tiles); the ring backward reserves min(2 GiB, that for the whole key sequence)
+    128-key tiles); the ring backward reserves min(8 GiB, that for the whole key sequence)
     for bf16 inputs and nothing for fp32."""
     lib = _lib()
     q, k = T(2, 100, 8, 64), T(2, 300, 2, 64)
@@ -197,7 +197,7 @@ def test_bwd_ds_bytes_and_ring_ds_region():
     big_q, big_k = T(1, 32768, 32, 128), T(1, 32768, 8, 128)
     fq, fk = f(big_q), f(big_k)
     assert lib.ra_ring_bwd_workspace_bytes(big_q, big_k, fq, fk, fk) - \
-        lib.ra_ring_bwd_workspace_bytes(fq, fk, fq, fk, fk) == 2 << 30
+        lib.ra_ring_bwd_workspace_bytes(fq, fk, fq, fk, fk) == 8 << 30
 
 
 def test_stored_ds_entry_points_refuse():

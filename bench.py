@@ -149,6 +149,25 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
     return t, f
 
 
+def image_dit_fwd(steps=20, warmup=3):
+    """The image-DiT inference workload (B1, S 4608, H 24, D 128, inputs N(0,1) x 0.5): the
+    forward ring sweep of the full query sequence over 4 chunks of 1152 keys, LSE-merged,
+    4*B*H*S*S*D flop per sweep."""
+    w = W.IMAGE_DIT_FWD
+    q, k, v, _ = W.make_inputs(w)
+    d = torch.device("cuda", 0)
+    q, k, v = (t.to(d) for t in (q, k, v))
+    ch = ra.Chunks(ra.split_sizes(w.S, w.n_chunks), list(range(w.n_chunks)))
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=d)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=d)
+    fws = torch.empty(q.numel() * 4 + 256, dtype=torch.uint8, device=d)
+    t = timed(lambda: ra.ring_fwd(q, k, v, ch, out=out, lse=lse, workspace=fws), steps, warmup)
+    f = 4.0 * w.B * w.Hq * w.S * w.S * w.D
+    return {"B": w.B, "S": w.S, "H": w.Hq, "D": w.D, "chunks": ra.split_sizes(w.S, w.n_chunks),
+            "ms_per_sweep": round(t * 1e3, 4), "tflops": round(f / t / 1e12, 2),
+            "pct_of_peak": round(100.0 * f / t / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 
 
@@ -262,6 +281,7 @@ def main():
     ap.add_argument("--no-full", action="store_true", help="skip the full-Q sweep (extra field)")
     ap.add_argument("--no-masked", action="store_true", help="skip the key-masked sweep (extra field)")
     ap.add_argument("--no-allgather", action="store_true", help="skip the single fused sweep (extra field)")
+    ap.add_argument("--no-image", action="store_true", help="skip the image-DiT forward sweep (extra field)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="only launch the dominant kernel (for hardware-counter runs)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -358,6 +378,9 @@ def main():
                             "fwd_tflops": round(ra_["f_f"] / ra_["t_fwd"] / 1e12, 2),
                             "bwd_tflops": round(ra_["f_b"] / ra_["t_bwd"] / 1e12, 2)}
         del ra_
+        torch.cuda.empty_cache()
+    if not args.no_image:
+        res["image_dit_fwd"] = image_dit_fwd()
         torch.cuda.empty_cache()
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
     print(json.dumps(res), flush=True)

@@ -14,7 +14,7 @@ import torch
 import context_attention_lse_kv_amd as ra
 import oracle
 import workloads as W
-from parity import BF16_TOL, dev, np64, rel
+from parity import BF16_TOL, LSE_TOL_BF16, dev, max_abs, np64, oracle_by_head, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -119,3 +119,34 @@ def test_stored_ds_masked_keys_store_zero_and_values_never_read():
     assert torch.equal(res[0], res2[0])
     assert torch.equal(res[1][gm], res2[1][gm]) and torch.equal(res[2][gm], res2[2][gm])
     assert not res2[1][dead].any() and not res2[2][dead].any()
+
+
+def test_ring_bwd_sweeps_query_slices_when_ds_exceeds_region():
+    """Full Q (32768 rows) against the whole 32k sequence as one chunk: its dS (64 GiB) is 8x
+    the region, so the ring backward runs the stored-dS route in 8 query slices of 4096 rows.
+    dQ on sampled rows against the oracle; dK/dV against the 8-chunk ring (one slice per
+    chunk), which reaches the same sums in another order."""
+    w = W.VIDEO_DIT_GQA
+    q, k, v, do = W.make_inputs(w)
+    d = dev()
+    gq, gk, gv, gdo = (x.to(d) for x in (q, k, v, do))
+    assert ra.bwd_ds_bytes(gq, gk) == 64 << 30  # 32768 x 32768 x 32 heads x 2 B
+    assert ra.ring_bwd_workspace_bytes(gq, gk, torch.float32, torch.float32) < (8 << 30) + (64 << 20)
+    one = ra.Chunks([w.S], [0])
+    out, lse = ra.ring_fwd(gq, gk, gv, one)
+    dq, dk, dv = ra.ring_bwd(gq, gk, gv, out, gdo, lse, one, grad_dtype=torch.float32)
+    eight = ra.Chunks(ra.split_sizes(w.S, w.n_chunks), list(range(w.n_chunks)))
+    out8, lse8 = ra.ring_fwd(gq, gk, gv, eight)
+    dq8, dk8, dv8 = ra.ring_bwd(gq, gk, gv, out8, gdo, lse8, eight, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in ((dk, dk8), (dv, dv8), (dq, dq8)):
+        r = ((a - b).norm() / b.norm()).item()
+        assert r < 5e-3, r
+    rows = torch.as_tensor(np.sort(np.random.default_rng(7).choice(w.S, 64, replace=False)))
+    heads = [3, 17, 30]
+    qn, kn, vn, don = (np64(t) for t in (q[:, rows], k, v, do[:, rows]))
+    ref = oracle_by_head(qn, kn, vn, don, heads)
+    sel = lambda t: np64(t.cpu()[:, rows][:, :, heads])
+    assert rel(sel(out), ref["out"]) <= BF16_TOL
+    assert max_abs(np64(lse.cpu()[:, heads][:, :, rows]), ref["lse"]) <= LSE_TOL_BF16
+    assert rel(sel(dq), ref["dq"]) <= BF16_TOL

@@ -288,8 +288,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         const int n0 = it * BN;
         const bool more = it + 1 < ntiles;
         const bool last = n0 + BN > p.Sk;
-        const uint64_t kl = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) >> (4 * hh) : 0;  // this tile's key bits
+        const uint64_t kall = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) : ~0ull;  // this tile's valid keys
+        const uint64_t kl = kall >> (4 * hh);
         if (more) issue(it + 1, buf ^ 1);
+        if (MASK && kall == 0) {  // every key of the tile masked: the tile adds nothing
+            if (more) wait_vmem();
+            __syncthreads();
+            return;
+        }
+        const bool dense = kall == ~0ull;  // no masked key in the tile (and none past the chunk)
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
         f32x16_t sacc[2];
@@ -311,9 +318,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         // masked keys get -inf
         auto block_max = [&](int kb2) {
             if (MASK) {
+                if (!dense) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (!key_bit(kl, kb2, r)) sacc[kb2][r] = -INFINITY;
+                    for (int r = 0; r < 16; ++r)
+                        if (!key_bit(kl, kb2, r)) sacc[kb2][r] = -INFINITY;
+                }
             } else if (last) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -848,8 +857,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
         const bool more = it + 1 < ntiles;
-        const uint64_t kl = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) >> (4 * hh) : 0;  // this tile's key bits
+        const uint64_t kall = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) : ~0ull;  // this tile's valid keys
+        const uint64_t kl = kall >> (4 * hh);
         if (more) issue(it + 1, buf ^ 1);
+        if (MASK && kall == 0) {  // every key of the tile masked: dS = 0, nothing to add
+            if (more) wait_vmem();
+            __syncthreads();
+            continue;
+        }
+        const bool dense = kall == ~0ull;
         const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
         const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
         f32x16_t sacc[2], dpacc[2];
@@ -878,7 +894,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdParams p) {
                 const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -lse2));
                 const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -lse2));
                 float d0 = p0 * (dpacc[t / 2][r] - dl), d1 = p1 * (dpacc[t / 2][r + 1] - dl);
-                if (MASK) {
+                if (MASK && !dense) {
                     d0 = key_bit(kl, t / 2, r) ? d0 : 0.f;
                     d1 = key_bit(kl, t / 2, r + 1) ? d1 : 0.f;
                 }

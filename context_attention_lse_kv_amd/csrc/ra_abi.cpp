@@ -572,9 +572,12 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
         // bf16: the dK/dV kernel stores dS, the dQ pass reads it back (no second S, dP);
         // query rows go in slices whose dS fits the region
         const int64_t per_tile = q->dtype == RA_BF16 ? ra::ds_bytes(q->B, q->H, 64, kc.S) : 0;
+        // rows per slice: the slice's dS fits the region, and one (batch, head) slab of it stays
+        // within the 2^31 bytes the dQ pass addresses with 32-bit buffer offsets
+        const int64_t slab_rows = per_tile == 0 ? 0 : 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, kc.S));
         const int32_t rows = per_tile == 0 || per_tile > ds_room
                                  ? 0
-                                 : (int32_t)std::min<int64_t>(64 * (ds_room / per_tile), (int64_t)q->S);
+                                 : (int32_t)std::min<int64_t>({64 * (ds_room / per_tile), slab_rows, (int64_t)q->S});
         // slices so thin that the dQ pass cannot fill the chip: recompute instead
         if (rows == 0 || (rows < q->S && ra::dqs_workgroups(q->B, q->H, rows) < kMinSliceWorkgroups)) {
             RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, km, scale, dq_acc, dkc, dvc, s));

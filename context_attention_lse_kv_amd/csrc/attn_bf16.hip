@@ -85,6 +85,14 @@ struct BwdParams {
     // query tile), ds_nkg groups x ds_nqt tiles per (batch, query head); null = none
     uint16_t* ds;
     int ds_nqt, ds_nkg;
+    // Final bf16 outputs written once instead of the fp32 accumulators (dK/dV of a chunk
+    // swept in one launch; dQ of the last chunk of a sweep), or null.  dq_read = 0: the
+    // dQ pass treats the fp32 accumulator as zero (first chunk of a sweep) and stores.
+    uint16_t* dk16;
+    uint16_t* dv16;
+    uint16_t* dq16;
+    int64_t dk16_sB, dk16_sS, dk16_sH, dv16_sB, dv16_sS, dv16_sH, dq16_sB, dq16_sS, dq16_sH;
+    int dq_read;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -748,6 +756,24 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         const uint32_t kbyte = load_key_byte(p.km + (int64_t)b * p.km_sB, p.Sk, n0 + 32 * kg, lane & 31);
         kl_own = __builtin_amdgcn_ballot_w64(kbyte != 0 && lane < 32) >> (4 * hh);
     }
+    if (p.dk16 != nullptr) {
+        // the launch sweeps every query row against this chunk: write the final bf16 rows
+        // (masked keys: zero) instead of adding to the fp32 accumulators
+        uint16_t* const dst16 = role == 0 ? p.dv16 + (int64_t)b * p.dv16_sB + (int64_t)g * p.dv16_sH + (int64_t)(n0 + 32 * kg + 4 * hh) * p.dv16_sS + l32
+                                          : p.dk16 + (int64_t)b * p.dk16_sB + (int64_t)g * p.dk16_sH + (int64_t)(n0 + 32 * kg + 4 * hh) * p.dk16_sS + l32;
+        const int64_t dst16_sS = role == 0 ? p.dv16_sS : p.dk16_sS;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kr = 8 * (r / 4) + (r % 4);
+                if (!keys_partial || n0 + 32 * kg + 4 * hh + kr < p.Sk) {
+                    const float x = key_bit(kl_own, 0, r) ? mul * acc[db][r] : 0.f;
+                    dst16[(int64_t)kr * dst16_sS + 32 * db] = (uint16_t)(pack_bf16x2(x, x) & 0xffffu);
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -1085,21 +1111,27 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
     }
     // dQ^T accumulator of query block qr: lane = query row 32 qr + (l32 with bits 2 and 3
     // swapped) of the tile, register r = d 32 db + 8 (r / 4) + 4 hh + r % 4
+    // dq_read = 0: the accumulator counts as zero; dq16: write the final bf16 rows instead
     const int rloc = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 #pragma unroll
     for (int qr = 0; qr < 2; ++qr) {
         const int row = qt * 64 + 32 * qr + rloc;
         if (row >= p.Sq) continue;
         float* dqrow = p.dq + (int64_t)b * p.dq_sB + (int64_t)row * p.dq_sS + (int64_t)h * p.dq_sH;
+        uint16_t* dq16row = p.dq16 ? p.dq16 + (int64_t)b * p.dq16_sB + (int64_t)row * p.dq16_sS + (int64_t)h * p.dq16_sH
+                                   : nullptr;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 f32x4_t* pq = (f32x4_t*)(dqrow + 32 * db + 8 * g4 + 4 * hh);
-                f32x4_t v4 = *pq;
+                f32x4_t v4 = p.dq_read ? *pq : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v4[j] += p.scale * acc[qr][db][4 * g4 + j];
-                *pq = v4;
+                if (dq16row)
+                    *(u32x2_t*)(dq16row + 32 * db + 8 * g4 + 4 * hh) = u32x2_t{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+                else
+                    *pq = v4;
             }
     }
 }
@@ -1169,13 +1201,17 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
     p.km_sB = 0;
     p.ds = nullptr;
     p.ds_nqt = p.ds_nkg = 0;
+    p.dk16 = p.dv16 = p.dq16 = nullptr;
+    p.dk16_sB = p.dk16_sS = p.dk16_sH = p.dv16_sB = p.dv16_sS = p.dv16_sH = p.dq16_sB = p.dq16_sS = p.dq16_sH = 0;
+    p.dq_read = 1;
     return p;
 }
 }  // namespace
 
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                                 const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
-                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s) {
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s,
+                                const ra_tensor* dk_out, const ra_tensor* dv_out) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, v, dout, lse, delta, scale);
     p.dk = (float*)dk_acc.data;
@@ -1189,6 +1225,12 @@ hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra
     p.ds = (uint16_t*)ds;
     p.ds_nqt = ds_query_tiles(q.S);
     p.ds_nkg = ds_key_groups(k.S);
+    if (dk_out && dv_out) {
+        p.dk16 = (uint16_t*)dk_out->data;
+        p.dv16 = (uint16_t*)dv_out->data;
+        p.dk16_sB = dk_out->sB; p.dk16_sS = dk_out->sS; p.dk16_sH = dk_out->sH;
+        p.dv16_sB = dv_out->sB; p.dv16_sS = dv_out->sS; p.dv16_sH = dv_out->sH;
+    }
     const unsigned nb = (unsigned)p.n_tiles * k.H * q.B;
     if (q.D == 64) bwd_kv_bf16_kernel<64><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
     else bwd_kv_bf16_kernel<128><<<nb, 64 * kBwdWaves * 2, 0, s>>>(p);
@@ -1218,11 +1260,16 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
 }
 
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
-                               const ra_tensor& dq_acc, hipStream_t s) {
+                               const ra_tensor& dq_acc, hipStream_t s, bool dq_read, const ra_tensor* dq_out) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, k, q, ra_lse{}, ra_lse{}, scale);
     p.dq = (float*)dq_acc.data;
     p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
+    p.dq_read = dq_read ? 1 : 0;
+    if (dq_out) {
+        p.dq16 = (uint16_t*)dq_out->data;
+        p.dq16_sB = dq_out->sB; p.dq16_sS = dq_out->sS; p.dq16_sH = dq_out->sH;
+    }
     p.ds = (uint16_t*)ds;
     p.ds_nqt = ds_query_tiles(q.S);
     p.ds_nkg = ds_key_groups(k.S);

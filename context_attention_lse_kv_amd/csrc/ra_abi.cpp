@@ -557,43 +557,69 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     void* const ds = p;
     const int64_t ds_room = (int64_t)ds_region_bytes(*q, *k);
 
-    RA_HIP(ra::launch_bwd_delta(*out, *dout, delta, s));
-    RA_HIP(ra::launch_zero_f32(dq_acc, s));
-    RA_HIP(ra::launch_zero_f32(dk_acc, s));
-    RA_HIP(ra::launch_zero_f32(dv_acc, s));
+    // Plan: per chunk, the stored-dS route with query slices of `rows` rows (the dS of a
+    // slice fits the region and one (batch, head) slab of it stays within the 2^31 bytes the
+    // dQ pass addresses with 32-bit buffer offsets), or the recompute route (rows = 0) when
+    // slices would be so thin that the dQ pass could not fill the chip.
+    struct Step {
+        int c;
+        int32_t rows;
+    };
+    std::vector<Step> steps;
     for (int i = 0; i < chunks->n; ++i) {
         const int c = chunks->order[i];
         if (chunks->len[c] == 0 || q->S == 0) continue;
+        const int64_t per_tile = q->dtype == RA_BF16 ? ra::ds_bytes(q->B, q->H, 64, chunks->len[c]) : 0;
+        const int64_t slab_rows = per_tile == 0 ? 0 : 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, chunks->len[c]));
+        int32_t rows = per_tile == 0 || per_tile > ds_room
+                           ? 0
+                           : (int32_t)std::min<int64_t>({64 * (ds_room / per_tile), slab_rows, (int64_t)q->S});
+        if (rows > 0 && rows < q->S && ra::dqs_workgroups(q->B, q->H, rows) < kMinSliceWorkgroups) rows = 0;
+        steps.push_back({c, rows});
+    }
+    // When every chunk takes the stored-dS route in one slice, each chunk's dK/dV rows are
+    // final after its one dK/dV launch and dQ after the last dQ pass: bf16 outputs are then
+    // written directly (no zeroing of the fp32 accumulators, no casts at the end).
+    bool single = !steps.empty();
+    for (const Step& st : steps) single = single && st.rows >= q->S;
+    const bool direct_kv = single && dk->dtype == RA_BF16 && dv->dtype == RA_BF16;
+    const bool direct_dq = single && dq->dtype == RA_BF16;
+
+    RA_HIP(ra::launch_bwd_delta(*out, *dout, delta, s));
+    if (!direct_dq) RA_HIP(ra::launch_zero_f32(dq_acc, s));
+    if (!direct_kv) {
+        RA_HIP(ra::launch_zero_f32(dk_acc, s));
+        RA_HIP(ra::launch_zero_f32(dv_acc, s));
+    }
+    for (size_t i = 0; i < steps.size(); ++i) {
+        const int c = steps[i].c;
+        const int32_t rows = steps[i].rows;
         const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);
         const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
         const ra_tensor dkc = seq_slice(dk_acc, chunks->start[c], chunks->len[c]);
         const ra_tensor dvc = seq_slice(dv_acc, chunks->start[c], chunks->len[c]);
         const ra::KeyMask km = key_mask(kmask, chunks->start[c]);
-        // bf16: the dK/dV kernel stores dS, the dQ pass reads it back (no second S, dP);
-        // query rows go in slices whose dS fits the region
-        const int64_t per_tile = q->dtype == RA_BF16 ? ra::ds_bytes(q->B, q->H, 64, kc.S) : 0;
-        // rows per slice: the slice's dS fits the region, and one (batch, head) slab of it stays
-        // within the 2^31 bytes the dQ pass addresses with 32-bit buffer offsets
-        const int64_t slab_rows = per_tile == 0 ? 0 : 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, kc.S));
-        const int32_t rows = per_tile == 0 || per_tile > ds_room
-                                 ? 0
-                                 : (int32_t)std::min<int64_t>({64 * (ds_room / per_tile), slab_rows, (int64_t)q->S});
-        // slices so thin that the dQ pass cannot fill the chip: recompute instead
-        if (rows == 0 || (rows < q->S && ra::dqs_workgroups(q->B, q->H, rows) < kMinSliceWorkgroups)) {
+        if (rows == 0) {
             RA_TRY(enqueue_bwd_chunk(*q, kc, vc, *dout, *lse, delta, km, scale, dq_acc, dkc, dvc, s));
             continue;
         }
+        // bf16: the dK/dV kernel stores dS, the dQ pass reads it back (no second S, dP)
+        const ra_tensor dko = seq_slice(*dk, chunks->start[c], chunks->len[c]);
+        const ra_tensor dvo = seq_slice(*dv, chunks->start[c], chunks->len[c]);
         for (int32_t r0 = 0; r0 < q->S; r0 += rows) {
             const int32_t n = std::min(rows, q->S - r0);
             const ra_tensor qs = seq_slice(*q, r0, n), dos = seq_slice(*dout, r0, n), dqs = seq_slice(dq_acc, r0, n);
             const ra_lse ls = rows_slice(*lse, r0, n), dls = rows_slice(delta, r0, n);
-            RA_HIP(ra::launch_bwd_dkdv_bf16(qs, kc, vc, dos, ls, dls, km, scale, dkc, dvc, ds, s));
-            RA_HIP(ra::launch_bwd_dqs_bf16(qs, kc, ds, scale, dqs, s));
+            const ra_tensor dqo = seq_slice(*dq, r0, n);
+            RA_HIP(ra::launch_bwd_dkdv_bf16(qs, kc, vc, dos, ls, dls, km, scale, dkc, dvc, ds, s,
+                                            direct_kv ? &dko : nullptr, direct_kv ? &dvo : nullptr));
+            RA_HIP(ra::launch_bwd_dqs_bf16(qs, kc, ds, scale, dqs, s, !(direct_dq && i == 0),
+                                           direct_dq && i + 1 == steps.size() ? &dqo : nullptr));
         }
     }
-    if (dq->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));
-    if (dk->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dk_acc, *dk, s));
-    if (dv->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(dv_acc, *dv, s));
+    if (dq->dtype == RA_BF16 && !direct_dq) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));
+    if (dk->dtype == RA_BF16 && !direct_kv) RA_HIP(ra::launch_cast_f32_to_bf16(dk_acc, *dk, s));
+    if (dv->dtype == RA_BF16 && !direct_kv) RA_HIP(ra::launch_cast_f32_to_bf16(dv_acc, *dv, s));
     return ok();
 }
 

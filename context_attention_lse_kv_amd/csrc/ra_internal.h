@@ -59,14 +59,19 @@ hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra
 // Backward chunk step, split: add this chunk's contribution to dk_acc/dv_acc, or to
 // dq_acc (all fp32).
 // ds: dS workspace of ds_bytes(q.B, q.H, q.S, k.S) bytes that receives this chunk
-// step's dS (bf16, zero for keys outside the chunk or masked), or null.
+// step's dS (bf16, zero for keys outside the chunk or masked), or null.  dk_out/dv_out
+// (bf16, the chunk's rows): when given, the launch's dK/dV are final and written there
+// instead of being added to dk_acc/dv_acc (which are then not touched).
 hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                                 const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
-                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s);
+                                const ra_tensor& dk_acc, const ra_tensor& dv_acc, void* ds, hipStream_t s,
+                                const ra_tensor* dk_out = nullptr, const ra_tensor* dv_out = nullptr);
 // dq_acc += scale dS K from the dS workspace written by launch_bwd_dkdv_bf16 for the same
-// q rows and chunk k.
+// q rows and chunk k.  dq_read = false: dq_acc counts as zero (it is only written);
+// dq_out (bf16): when given, the sum is final and written there instead of dq_acc.
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
-                               const ra_tensor& dq_acc, hipStream_t s);
+                               const ra_tensor& dq_acc, hipStream_t s, bool dq_read = true,
+                               const ra_tensor* dq_out = nullptr);
 hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                               const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
                               const ra_tensor& dq_acc, hipStream_t s);

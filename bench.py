@@ -111,8 +111,8 @@ def run_workload(full, steps, warmup, masked=False, single=False):
 
 def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
     """The dK/dV half of the backward chunk step as the ring backward runs it (one
-    kernel launch per call with accumulate=1, which skips the zero fill; it also stores
-    the step's dS for the dQ pass).  It executes S = Q K^T, dP = dO V^T, dV = P^T dO and
+    kernel launch per call: it stores the step's dS for the dQ pass and writes the
+    chunk's final bf16 dK/dV rows).  It executes S = Q K^T, dP = dO V^T, dV = P^T dO and
     dK = dS^T Q: 8*D flop per (query row, key) pair per head.
 
     Each timed launch runs where it runs in the backward sweep: after the previous
@@ -127,8 +127,9 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
     kc, vc = k[:, :c], v[:, :c]
     delta = torch.empty_like(lse)
     ra.bwd_delta(out, do, delta)
-    dk = torch.zeros(kc.shape, dtype=torch.float32, device=q.device)
-    dv = torch.zeros_like(dk)
+    # bf16 dk/dv with accumulate = 0: the kernel writes the chunk's final rows, as in the ring
+    dk = torch.empty(kc.shape, dtype=torch.bfloat16, device=q.device)
+    dv = torch.empty_like(dk)
     dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
     ds = torch.empty(ra.bwd_ds_bytes(q, kc), dtype=torch.uint8, device=q.device)
     w = r["w"]
@@ -142,7 +143,7 @@ def dominant_kernel(r, launches=8, back_to_back=False, lead_steps=3):
         if not back_to_back:
             ra.bwd_chunk_dq_ds(q, kc, ds, dq)
         ev[i][0].record(s)
-        ra.bwd_chunk_dkdv_ds(q, kc, vc, do, lse, delta, dk, dv, 1, ds)
+        ra.bwd_chunk_dkdv_ds(q, kc, vc, do, lse, delta, dk, dv, 0, ds)
         ev[i][1].record(s)
     torch.cuda.synchronize()
     t = sum(a.elapsed_time(b) for a, b in ev) / launches / 1e3

@@ -421,18 +421,30 @@ ra_status ra_bwd_chunk_dkdv_ds(const ra_tensor* q, const ra_tensor* k, const ra_
                                void* stream) {
     RA_TRY(check_bwd_chunk(q, k, v, dout, lse, delta, scale));
     RA_TRY(check_kmask(kmask, q->B, k->S));
-    RA_TRY(check_acc(dk_acc, "dk_acc", *k));
-    RA_TRY(check_acc(dv_acc, "dv_acc", *k));
     if (accumulate != 0 && accumulate != 1) return fail(RA_E_ARG, "accumulate must be 0 or 1");
+    // bf16 dk/dv: the step's dK/dV are final and written there (accumulate must be 0)
+    const bool direct = dk_acc && dv_acc && dk_acc->dtype == RA_BF16 && dv_acc->dtype == RA_BF16;
+    if (direct) {
+        RA_TRY(check_tensor(dk_acc, "dk_acc"));
+        RA_TRY(check_tensor(dv_acc, "dv_acc"));
+        if (!same_shape(*dk_acc, *k) || !same_shape(*dv_acc, *k)) return fail(RA_E_SHAPE, "dk/dv: shape does not match");
+        if (accumulate) return fail(RA_E_DTYPE, "bf16 dk/dv are written, not accumulated: accumulate must be 0");
+    } else {
+        RA_TRY(check_acc(dk_acc, "dk_acc", *k));
+        RA_TRY(check_acc(dv_acc, "dv_acc", *k));
+    }
     RA_TRY(check_ds(*q, *k, ds, ds_bytes));
     hipStream_t s = (hipStream_t)stream;
-    if (!accumulate) {
+    if (!accumulate && !direct) {
         RA_HIP(ra::launch_zero_f32(*dk_acc, s));
         RA_HIP(ra::launch_zero_f32(*dv_acc, s));
     }
     if (k->S > 0 && q->S > 0)
         RA_HIP(ra::launch_bwd_dkdv_bf16(*q, *k, *v, *dout, *lse, *delta, key_mask(kmask), scale, *dk_acc, *dv_acc,
-                                        ds, s));
+                                        ds, s, direct ? dk_acc : nullptr, direct ? dv_acc : nullptr));
+    else if (direct && k->S > 0) {
+        return fail(RA_E_UNSUPPORTED, "bf16 dk/dv with no query rows: nothing would write them (use fp32)");
+    }
     return ok();
 }
 

@@ -196,8 +196,12 @@ ra_status ra_bwd_chunk_dq_masked(const ra_tensor* q, const ra_tensor* k, const r
  * buffer ds; ra_bwd_chunk_dq_ds then adds scale dS K to dq_acc (fp32) from that
  * buffer, with the same q (rows), k (chunk) and scale, without forming S and dP
  * again.  ds must hold ra_bwd_ds_bytes(q, k) bytes (256-byte aligned); its
- * layout is private to these two calls.  bf16 only (RA_E_DTYPE otherwise);
- * ds too small or NULL: RA_E_WORKSPACE.  The result equals ra_bwd_chunk's up
+ * layout is private to these two calls.  dk_acc/dv_acc may also be bf16
+ * (shape of k) with accumulate = 0: the step's dK/dV are then final and
+ * written there in bf16 (what ra_ring_bwd does when each chunk is one step;
+ * with S_q = 0 that is refused, RA_E_UNSUPPORTED, as nothing would write
+ * them).  bf16 inputs only (RA_E_DTYPE otherwise); ds too small or NULL:
+ * RA_E_WORKSPACE.  The result equals ra_bwd_chunk's up
  * to rounding (P reaches dS through fp16 here). */
 size_t ra_bwd_ds_bytes(const ra_tensor* q, const ra_tensor* k);
 ra_status ra_bwd_chunk_dkdv_ds(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,

@@ -222,6 +222,9 @@ def test_stored_ds_entry_points_refuse():
     assert kv(FAKE, need, acc=T(1, 64, 2, 64)) == abi.RA_E_DTYPE
     q32, k32 = T(1, 64, 8, 64, abi.RA_F32), T(1, 64, 2, 64, abi.RA_F32)
     assert kv(FAKE, need, q=q32, k=k32, v=k32) == abi.RA_E_DTYPE
+    # bf16 dk/dv are final outputs: only with accumulate = 0, and of the shape of k
+    assert kv(FAKE, need, acc=T(1, 64, 2, 64), acc_v=T(1, 64, 2, 64), accumulate=1) == abi.RA_E_DTYPE
+    assert kv(FAKE, need, acc=T(1, 64, 2, 128), acc_v=T(1, 64, 2, 128), accumulate=0) == abi.RA_E_SHAPE
     assert lib.ra_bwd_chunk_dq_ds(q, k, None, 0, 0.125, acc_q, None) == abi.RA_E_WORKSPACE
     assert lib.ra_bwd_chunk_dq_ds(q, k, FAKE, need - 256, 0.125, acc_q, None) == abi.RA_E_WORKSPACE
     assert lib.ra_bwd_chunk_dq_ds(q, T(1, 64, 3, 64), FAKE, need, 0.125, acc_q, None) == abi.RA_E_SHAPE

@@ -150,3 +150,29 @@ def test_ring_bwd_sweeps_query_slices_when_ds_exceeds_region():
     assert rel(sel(out), ref["out"]) <= BF16_TOL
     assert max_abs(np64(lse.cpu()[:, heads][:, :, rows]), ref["lse"]) <= LSE_TOL_BF16
     assert rel(sel(dq), ref["dq"]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_direct_bf16_dkdv_equals_accumulate_then_cast(case):
+    """bf16 dk/dv with accumulate = 0 are written directly by the kernel; they equal the fp32
+    accumulate path cast to bf16 bit for bit (0 + x = x, both round the same fp32 value)."""
+    name, B, S, Sq, Hq, Hkv, D, lens, order, recipe = case
+    q, k, v, do, m = _inputs(case)
+    d = dev()
+    gq, gk, gv, gdo = (x.to(d) for x in (q, k, v, do))
+    gm = None if m is None else m.to(d)
+    out, lse = ra.ring_fwd(gq, gk, gv, ra.Chunks(lens, order), kmask=gm)
+    delta = torch.empty_like(lse)
+    ra.bwd_delta(out, gdo, delta)
+    c = lens[0]
+    kc, vc = gk[:, :c], gv[:, :c]
+    km = None if gm is None else gm[:, :c]
+    ds = torch.empty(ra.bwd_ds_bytes(gq, kc), dtype=torch.uint8, device=d)
+    dk32 = torch.empty(kc.shape, dtype=torch.float32, device=d)
+    dv32 = torch.empty_like(dk32)
+    ra.bwd_chunk_dkdv_ds(gq, kc, vc, gdo, lse, delta, dk32, dv32, 0, ds, kmask=km)
+    dk16 = torch.full(kc.shape, float("nan"), dtype=torch.bfloat16, device=d)
+    dv16 = torch.full_like(dk16, float("nan"))
+    ra.bwd_chunk_dkdv_ds(gq, kc, vc, gdo, lse, delta, dk16, dv16, 0, ds, kmask=km)
+    torch.cuda.synchronize()
+    assert torch.equal(dk16, dk32.to(torch.bfloat16)) and torch.equal(dv16, dv32.to(torch.bfloat16))

@@ -61,6 +61,8 @@ struct FwdParams {
     float c;                    // scale * log2(e)
     const uint8_t* km;          // key mask of the chunk (km[b * km_sB + key] != 0: key takes part), or null
     int64_t km_sB;
+    uint16_t* out16;            // the sweep's last step: final bf16 output written here instead of out, or null
+    int64_t o16_sB, o16_sS, o16_sH;
 };
 
 struct BwdParams {
@@ -416,14 +418,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     if (!row_ok) return;
     float* orow = p.out + (int64_t)b * p.o_sB + (int64_t)row * p.o_sS + (int64_t)h * p.o_sH;
     float* lp = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row;
+    // the output of the sweep's last step goes straight to the final bf16 tensor (rounded to
+    // nearest even, as the cast it replaces would)
+    uint16_t* o16row = p.out16 ? p.out16 + (int64_t)b * p.o16_sB + (int64_t)row * p.o16_sS + (int64_t)h * p.o16_sH
+                               : nullptr;
+    auto put = [&](int db, int g4, const f32x4_t& v4) {
+        if (o16row)
+            *(u32x2_t*)(o16row + 32 * db + 8 * g4 + 4 * hh) = u32x2_t{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+        else
+            *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = v4;
+    };
     if (MASK && l == 0.f) {
-        // every key of the chunk masked: the step's partial is the merge identity
+        // every key of the chunk masked: the step's partial is the merge identity (a merge
+        // leaves the running state as it is; only a final bf16 output must still be written)
         if (!MERGE) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int g4 = 0; g4 < 4; ++g4) put(db, g4, f32x4_t{0.f, 0.f, 0.f, 0.f});
             if (hh == 0) *lp = -INFINITY;
+        } else if (o16row) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) put(db, g4, *(const f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh));
         }
         return;
     }
@@ -436,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
             for (int g4 = 0; g4 < 4; ++g4) {
                 const f32x4_t v4 = {oacc[db][4 * g4] * inv_l, oacc[db][4 * g4 + 1] * inv_l,
                                     oacc[db][4 * g4 + 2] * inv_l, oacc[db][4 * g4 + 3] * inv_l};
-                *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = v4;
+                put(db, g4, v4);
             }
         if (hh == 0) *lp = lse_c;
     } else {
@@ -450,12 +468,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                f32x4_t* po = (f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh);
-                const f32x4_t old = *po;
+                const f32x4_t old = *(const f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh);
                 f32x4_t v4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v4[j] = (wa == 0.f ? 0.f : wa * old[j]) + wc * oacc[db][4 * g4 + j];
-                *po = v4;
+                put(db, g4, v4);
             }
         if (hh == 0) *lp = mm + logf(sum);
     }
@@ -1139,7 +1156,8 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
 }  // namespace
 
 hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
-                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s,
+                                 const ra_tensor* out16) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     FwdParams p;
     p.q = (const uint16_t*)q.data;
@@ -1160,6 +1178,10 @@ hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     const unsigned nb = (unsigned)p.n_qtiles * q.H * q.B;
     p.km = km.data;
     p.km_sB = km.sB;
+    p.out16 = out16 ? (uint16_t*)out16->data : nullptr;
+    p.o16_sB = out16 ? out16->sB : 0;
+    p.o16_sS = out16 ? out16->sS : 0;
+    p.o16_sH = out16 ? out16->sH : 0;
     const bool mk = km.data != nullptr;
     if (q.D == 64) {
         if (merge) mk ? fwd_bf16_kernel<64, true, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<64, true, false><<<nb, 256, 0, s>>>(p);

@@ -236,7 +236,8 @@ ra::KeyMask key_mask(const ra_kmask* m, int32_t start = 0) {
 }
 
 ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra::KeyMask& km,
-                            float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s) {
+                            float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s,
+                            const ra_tensor* out16 = nullptr) {
     if (k.S == 0) {
         if (!merge) {  // the partial of an empty chunk is the merge identity
             RA_HIP(ra::launch_zero_f32(out, s));
@@ -244,7 +245,7 @@ ra_status enqueue_fwd_chunk(const ra_tensor& q, const ra_tensor& k, const ra_ten
         }
         return RA_OK;
     }
-    if (q.dtype == RA_BF16) RA_HIP(ra::launch_fwd_chunk_bf16(q, k, v, km, scale, out, lse, merge, s));
+    if (q.dtype == RA_BF16) RA_HIP(ra::launch_fwd_chunk_bf16(q, k, v, km, scale, out, lse, merge, s, out16));
     else RA_HIP(ra::launch_fwd_chunk_f32(q, k, v, km, scale, out, lse, merge, s));
     return RA_OK;
 }
@@ -522,13 +523,19 @@ ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     RA_TRY(check_ws(ws, ws_bytes, need));
     hipStream_t s = (hipStream_t)stream;
     const ra_tensor acc = out->dtype == RA_F32 ? *out : contiguous_f32(ws, *q);
+    // A bf16 sweep's last non-empty step writes the final bf16 output itself (no cast pass).
+    int last = -1;
+    if (q->dtype == RA_BF16 && out->dtype == RA_BF16 && q->S > 0)
+        for (int i = 0; i < chunks->n; ++i)
+            if (chunks->len[chunks->order[i]] > 0) last = i;
     for (int i = 0; i < chunks->n; ++i) {
         const int c = chunks->order[i];
         const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);
         const ra_tensor vc = seq_slice(*v, chunks->start[c], chunks->len[c]);
-        RA_TRY(enqueue_fwd_chunk(*q, kc, vc, key_mask(kmask, chunks->start[c]), scale, acc, *lse, i > 0 ? 1 : 0, s));
+        RA_TRY(enqueue_fwd_chunk(*q, kc, vc, key_mask(kmask, chunks->start[c]), scale, acc, *lse, i > 0 ? 1 : 0, s,
+                                 i == last ? out : nullptr));
     }
-    if (out->dtype == RA_BF16) RA_HIP(ra::launch_cast_f32_to_bf16(acc, *out, s));
+    if (out->dtype == RA_BF16 && last < 0) RA_HIP(ra::launch_cast_f32_to_bf16(acc, *out, s));
     return ok();
 }
 

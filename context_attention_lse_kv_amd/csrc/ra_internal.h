@@ -52,8 +52,11 @@ struct PermuteTable {
 
 // All launchers enqueue on `s` and return hipGetLastError() of the launch.
 // Shapes have been validated by the caller.
+// out16 (bf16, shape of q): when given, the step is the sweep's last and its (merged)
+// output is written there in bf16 instead of to out; lse is written as usual.
 hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
-                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
+                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s,
+                                 const ra_tensor* out16 = nullptr);
 hipError_t launch_fwd_chunk_f32(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const KeyMask& km,
                                 float scale, const ra_tensor& out, const ra_lse& lse, int merge, hipStream_t s);
 // Backward chunk step, split: add this chunk's contribution to dk_acc/dv_acc, or to

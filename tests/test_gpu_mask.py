@@ -165,6 +165,27 @@ def test_masked_chunk_entry_points_match_ring():
     assert rel < 5e-3, rel
 
 
+@pytest.mark.parametrize("lens,order,masked", [
+    ((192, 192), (0, 1), [(0, 192, 384)]),      # batch 0: every key of the last chunk masked
+    ((192, 0, 192), (2, 0, 1), [(1, 0, 192)]),  # last chunk in order empty, batch 1's keys of the one before masked
+    ((384,), (0,), [(0, 0, 384)]),              # one chunk, batch 0 without a valid key
+])
+def test_masked_bf16_output_is_rne_of_fp32(lens, order, masked):
+    """The bf16 output that the sweep's last non-empty step writes itself equals the fp32
+    output rounded to nearest even, also for rows whose keys in that step are all masked."""
+    B, S, Sq, Hq, Hkv, D = 2, 384, 150, 4, 2, 128
+    q, k, v = (W.randn(s, 995 + i, "bf16") for i, s in enumerate([(B, Sq, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D)]))
+    m = W.make_key_mask(B, S, 999, p_keep=0.8, masked_ranges=masked)
+    d = dev()
+    gq, gk, gv, gm = (x.to(d) for x in (q, k, v, m))
+    ch = ra.Chunks(lens, order)
+    o32, l32 = ra.ring_fwd(gq, gk, gv, ch, kmask=gm, out_dtype=torch.float32)
+    o16, l16 = ra.ring_fwd(gq, gk, gv, ch, kmask=gm, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16)) and torch.equal(l16, l32)
+    assert not torch.isnan(o16).any()
+
+
 def test_masked_video_shard():
     """The video-DiT GQA rank-0 shard with right padding (valid 30000 of 32768 keys) and
     5 % of the other keys masked; oracle on two kv-head groups."""

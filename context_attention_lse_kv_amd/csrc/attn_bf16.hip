@@ -49,6 +49,16 @@ typedef RA_LDS uint16_t lds_u16;
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold of the running max, in log2 units
 
+// f(std::integral_constant<int, I>) for I = B .. E - 1, as straight-line code (the
+// indices are compile-time constants inside f).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 struct FwdParams {
     const uint16_t* q;
     const uint16_t* k;
@@ -209,6 +219,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
     constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
     constexpr int RPI = 1024 / ROWB, NI = BN / RPI / 4;
+    constexpr int NSS = 2 * KS, NPV = 4 * DB;  // S^T and P V MFMAs per tile
     static_assert(RC >= 8 && NI >= 1, "tile geometry");
     __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [K0 | V0 | K1 | V1]
     RA_LDS char* const lbase = (RA_LDS char*)smem;
@@ -247,19 +258,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         vv[i] = copy_voff<D>(w * NI + i, lane, p.v_sS);
     }
     const uint8_t* km_b = MASK ? p.km + (int64_t)b * p.km_sB : nullptr;
-    uint32_t kbyte = 0;  // mask byte of key n0 + lane of the tile in flight
-    auto issue = [&](int it, int buf) {
-        const int r0 = it * BN;
-        const i32x4_t rk = tile_desc(kbase, r0, p.k_sS * 2, p.k_bytes);
-        const i32x4_t rv = tile_desc(vbase, r0, p.v_sS * 2, p.v_bytes);
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    // LDS: [K0 | V0 | K1 | V1]; K and V tile it live in buffer it & 1.  With the key mask,
+    // kbyte[buf] is the mask byte of key (tile start + lane) of the K tile in that buffer.
+    uint32_t kbyte[2] = {0u, 0u};
+    auto issue_k = [&](int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        const i32x4_t rk = tile_desc(kbase, it * BN, p.k_sS * 2, p.k_bytes);
         RA_LDS char* kdst = lbase + (2 * buf) * TILEB;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
+        if (MASK) kbyte[buf] = load_key_byte(km_b, p.Sk, it * BN, lane);
+    };
+    auto issue_v = [&](int it, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        const i32x4_t rv = tile_desc(vbase, it * BN, p.v_sS * 2, p.v_bytes);
         RA_LDS char* vdst = lbase + (2 * buf + 1) * TILEB;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
-            dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
-        }
-        if (MASK) kbyte = load_key_byte(km_b, p.Sk, r0, lane);
+        for (int i = 0; i < NI; ++i) dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
     };
     // lane-constant LDS offsets: K row reads (S^T operand) and transposing V reads (V^T operand)
     const int sw_row = swz<RC>(l32);
@@ -273,145 +290,192 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         tr_off[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr) + 8 * (a4 & 1);
         tr_off8[db] = (4 * hh + e4) * ROWB + 16 * ((4 * db + 2 * (gq & 1) + (a4 >> 1)) ^ sw_tr8) + 8 * (a4 & 1);
     }
-
-    issue(0, 0);
-    wait_vmem();
-    __syncthreads();
-    // One key tile is a software pipeline of single-MFMA slots: slots [0, NSS) compute
-    // S^T of key block kb2 = s / KS at k-step s % KS, slots [NSS, NSLOT) add V^T P^T for
-    // 16 keys t and column block db.  Row reads run PF slots and transposing reads LT
-    // slots ahead of their MFMAs; each 32-key block gets its own max and exponentials two
-    // slots after its last S^T MFMA, so the softmax of block 0 overlaps the MFMAs of
-    // block 1 and that of block 1 the first P V MFMAs.  A scheduling barrier closes
-    // every slot.
-    //   The running max moves lazily (only when a block exceeds it by more than
-    // kRescale, in log2 units).  A move triggered by block 1 rescales l at once but the
-    // O accumulator only after the P V MFMAs of block 0, which still use the old max.
-    //   With a key mask, masked keys get s = -inf; a row that has seen no valid key yet
-    // keeps m = -inf and takes its exponentials against 0 (all its scores are -inf).
-    constexpr int NSS = 2 * KS, NSLOT = NSS + 4 * DB;
-    constexpr int PF = 4, LT = 2;
-    const int ntiles = (p.Sk + BN - 1) / BN;
-    // the loop body per buffer parity, so that the LDS addresses fold into immediates
-    auto tile = [&](const int it, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        const int n0 = it * BN;
-        const bool more = it + 1 < ntiles;
-        const bool last = n0 + BN > p.Sk;
-        const uint64_t kall = MASK ? __builtin_amdgcn_ballot_w64(kbyte != 0) : ~0ull;  // this tile's valid keys
-        const uint64_t kl = kall >> (4 * hh);
-        if (more) issue(it + 1, buf ^ 1);
-        if (MASK && kall == 0) {  // every key of the tile masked: the tile adds nothing
-            if (more) wait_vmem();
-            __syncthreads();
-            return;
-        }
-        const bool dense = kall == ~0ull;  // no masked key in the tile (and none past the chunk)
-        const RA_LDS char* kb = lbase + (2 * buf) * TILEB;
-        const RA_LDS char* vb = lbase + (2 * buf + 1) * TILEB;
-        f32x16_t sacc[2];
-        bf16x8_t stk[NSS];
-        u32x4_t pk[4];
-        u32x2_t trv[4 * DB][2];
-        float alpha1 = 1.f;
-        bool late = false;
-
-        auto row_read = [&](int i) {
-            stk[i] = lds_b128((const lds_u16*)(kb + (i / KS) * 32 * ROWB + ra_off[i % KS]));
-        };
-        auto tr_read = [&](int j) {  // V^T operand of slot NSS + j: keys 16 t .. 16 t + 15
-            const int t = j / DB, db = j % DB;
-            trv[j][0] = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
-            trv[j][1] = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
-        };
-        // max of key block kb2 in log2 units; keys past the chunk (read as zero) and
-        // masked keys get -inf
-        auto block_max = [&](int kb2) {
-            if (MASK) {
-                if (!dense) {
+    auto k_read = [&](const RA_LDS char* kb, int i) {  // K rows of S^T MFMA i: key block i / KS, k-step i % KS
+        return lds_b128((const lds_u16*)(kb + (i / KS) * 32 * ROWB + ra_off[i % KS]));
+    };
+    auto v_read = [&](const RA_LDS char* vb, int j, u32x2_t (&dst)[2]) {  // V^T operand of P V MFMA j
+        const int t = j / DB, db = j % DB;
+        dst[0] = lds_tr((const lds_u16*)(vb + 16 * t * ROWB + tr_off[db]));
+        dst[1] = lds_tr((const lds_u16*)(vb + (16 * t + 8) * ROWB + tr_off8[db]));
+    };
+    // Max of a tile's scores (both 32-key blocks) in log2 units, over the lane pair that
+    // shares a query row.  Masked keys and keys past the chunk (`tail`: their K rows
+    // read as zero) count as -inf and are set to -inf for the exponentials.
+    auto tile_max = [&](f32x16_t (&sc)[2], uint32_t kby, int n0, bool tail) {
+        if (MASK) {
+            const uint64_t kall = __builtin_amdgcn_ballot_w64(kby != 0);
+            if (kall != ~0ull) {
+                const uint64_t kl = kall >> (4 * hh);
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (!key_bit(kl, kb2, r)) sacc[kb2][r] = -INFINITY;
-                }
-            } else if (last) {
+                        if (!key_bit(kl, kb2, r)) sc[kb2][r] = -INFINITY;
+            }
+        } else if (tail) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sacc[kb2][r] = -INFINITY;
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
-            return half_max(mx) * p.c;
-        };
-        auto exps = [&](int t) {  // P^T of keys 16 t .. 16 t + 15 as the B operand
-            const float ms = MASK && m == -INFINITY ? 0.f : m;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 8 * (t % 2) + 2 * j;
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r], p.c, -ms));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t / 2][r + 1], p.c, -ms));
-                l += p0 + p1;
-                pk[t][j] = pack_bf16x2(p0, p1);
-            }
-        };
-
-#pragma unroll
-        for (int i = 0; i < PF; ++i) row_read(i);
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-            if (s < NSS) {
-                const int kb2 = s / KS, ks = s % KS;
-                sacc[kb2] = mfma32(stk[s], qreg[ks], ks == 0 ? f32x16_t{} : sacc[kb2]);
-                if (s + PF < NSS) row_read(s + PF);
-            } else {
-                const int j = s - NSS, t = j / DB, db = j % DB;
-                if (j == 2 * DB && late) {
-#pragma unroll
-                    for (int d2 = 0; d2 < DB; ++d2)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[d2][r] *= alpha1;
-                }
-                oacc[db] = mfma32(as_bf16x8(u32x4_t{trv[j][0][0], trv[j][0][1], trv[j][1][0], trv[j][1][1]}),
-                                  as_bf16x8(pk[t]), oacc[db]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4 * DB; ++j)
-                if (s == NSS + j - LT) tr_read(j);
-            if (s == KS + 2) {
-                const float mx = block_max(0);
-                if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
-                    const float m_new = fmaxf(m, mx);
-                    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-                    l *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                    m = m_new;
-                }
-                exps(0);
-            }
-            if (s == KS + 3) exps(1);
-            if (s == NSS + 1) {
-                const float mx = block_max(1);
-                if (__builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0) {
-                    const float m_new = fmaxf(m, mx);
-                    alpha1 = __builtin_amdgcn_exp2f(m - m_new);
-                    l *= alpha1;
-                    m = m_new;
-                    late = true;
-                }
-            }
-            if (s == NSS + 2) exps(2);
-            if (s == NSS + 3) exps(3);
-            __builtin_amdgcn_sched_barrier(0);
+                    if (n0 + kb2 * 32 + 8 * (r / 4) + 4 * hh + (r % 4) >= p.Sk) sc[kb2][r] = -INFINITY;
         }
-        if (more) wait_vmem();
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
+        return half_max(mx) * p.c;
+    };
+    // Lazy move of the running max (only when some row of the wavefront grows by more
+    // than kRescale): rescales l at once and returns the factor the output accumulator
+    // still has to take (1 when the max stays); `moved` (uniform) tells whether it moved.
+    // Branch-free: the decision is a wavefront-uniform select.
+    bool moved = false;
+    auto move_max = [&](float mx) {
+        moved = __builtin_amdgcn_ballot_w64(mx > m + kRescale) != 0;
+        const float m_new = moved ? fmaxf(m, mx) : m;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        l *= alpha;
+        m = m_new;
+        return alpha;
+    };
+    // Exponentials of scores 2 j, 2 j + 1 of 16-key unit t (keys 16 t .. 16 t + 15), packed
+    // as bf16 into the P^T operand of the P V MFMAs of that unit
+    auto exp_pair = [&](const f32x16_t (&sc)[2], int t, int j, u32x4_t& pkt) {
+        const float ms = MASK && m == -INFINITY ? 0.f : m;  // row without a valid key yet
+        const int r = 8 * (t % 2) + 2 * j;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t / 2][r], p.c, -ms));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t / 2][r + 1], p.c, -ms));
+        l += p0 + p1;
+        pkt[j] = pack_bf16x2(p0, p1);
+        // keep the pair in its slot: otherwise the compiler sinks the exponentials and the
+        // running sum behind the (rare) output-rescale branch that follows the slots
+        asm volatile("" ::"v"(pkt[j]), "v"(l));
+    };
+    auto s_tile = [&](const RA_LDS char* kb, f32x16_t (&sc)[2]) {  // S^T of a whole tile, not pipelined
+#pragma unroll
+        for (int i = 0; i < NSS; ++i) sc[i / KS] = mfma32(k_read(kb, i), qreg[i % KS], i % KS == 0 ? f32x16_t{} : sc[i / KS]);
+    };
+    auto pv_tile = [&](const RA_LDS char* vb, const u32x4_t (&pk)[4]) {  // O^T += V^T P^T of a whole tile
+#pragma unroll
+        for (int j = 0; j < NPV; ++j) {
+            u32x2_t tv[2];
+            v_read(vb, j, tv);
+            oacc[j % DB] = mfma32(as_bf16x8(u32x4_t{tv[0][0], tv[0][1], tv[1][0], tv[1][1]}), as_bf16x8(pk[j / DB]),
+                                  oacc[j % DB]);
+        }
+    };
+    auto rescale_out = [&](float alpha) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    };
+
+    // Software pipeline over the chunk's full key tiles: iteration T forms P of tile T
+    // (its scores S(T) and its max were produced by iteration T - 1), computes the scores
+    // S(T + 1) of the next tile and adds V^T P^T of tile T.  Slots [0, NSS) run the
+    // S(T + 1) MFMAs with the exponentials of units 1..3 of tile T between them; slots
+    // [NSS, NSS + NPV) run the P V MFMAs of tile T with the max of tile T + 1, the move
+    // of the running max and the exponentials of unit 0 of tile T + 1 between them (the
+    // output accumulator takes a move's factor after the last P V MFMA).  The slot
+    // region has no branch, so the compiler keeps every piece in its slot; a
+    // scheduling barrier closes each slot.  K tile T + 2 and V tile T + 1 are copied
+    // during iteration T (one barrier per iteration).  A partial last tile runs after
+    // the loop without pipelining.
+    const int nfull = p.Sk / BN, ntiles = (p.Sk + BN - 1) / BN;
+    issue_k(0, B0{});
+    issue_v(0, B0{});
+    if (ntiles > 1) issue_k(1, B1{});
+    wait_vmem();
+    __syncthreads();
+    f32x16_t sc[2];   // scores of the tile whose P is being formed
+    u32x4_t pk[4];    // its P^T operands
+    if (nfull > 0) {
+        s_tile(lbase, sc);
+        const float alpha = move_max(tile_max(sc, kbyte[0], 0, false));
+        (void)alpha;  // the output accumulator is still zero
+#pragma unroll
+        for (int j = 0; j < 4; ++j) exp_pair(sc, 0, j, pk[0]);
+    }
+    __syncthreads();  // K tile 0 read by everyone before its buffer takes tile 2
+
+    constexpr int PF = 4, LT = 2;
+    auto iteration = [&](const int T, auto bufc, auto nextc) {
+        constexpr int cb = decltype(bufc)::value, nb = cb ^ 1;
+        constexpr bool NEXT = decltype(nextc)::value;  // tile T + 1 is a full tile
+        if (T + 2 < ntiles) issue_k(T + 2, bufc);
+        if (T + 1 < ntiles) issue_v(T + 1, std::integral_constant<int, nb>{});
+        const RA_LDS char* kb = lbase + (2 * nb) * TILEB;      // K of tile T + 1
+        const RA_LDS char* vb = lbase + (2 * cb + 1) * TILEB;  // V of tile T
+        f32x16_t sn[2];
+        bf16x8_t stk[NSS];
+        u32x2_t trv[NPV][2];
+        u32x4_t pk0n;
+        float alpha = 1.f;
+        if constexpr (NEXT) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) stk[i] = k_read(kb, i);
+        }
+        static_for<0, NSS + NPV>([&](auto sc_) {
+            constexpr int s = decltype(sc_)::value;
+            if constexpr (s < NSS) {
+                if constexpr (NEXT) {
+                    sn[s / KS] = mfma32(stk[s], qreg[s % KS], s % KS == 0 ? f32x16_t{} : sn[s / KS]);
+                    if constexpr (s + PF < NSS) stk[s + PF] = k_read(kb, s + PF);
+                }
+                // exponentials of units 1..3 of tile T: 12 pairs spread over the S slots
+                static_for<0, 12>([&](auto uc) {
+                    constexpr int u = decltype(uc)::value;
+                    if constexpr (u * NSS / 12 == s) exp_pair(sc, 1 + u / 4, u % 4, pk[1 + u / 4]);
+                });
+            } else {
+                constexpr int j = s - NSS;
+                oacc[j % DB] = mfma32(as_bf16x8(u32x4_t{trv[j][0][0], trv[j][0][1], trv[j][1][0], trv[j][1][1]}),
+                                      as_bf16x8(pk[j / DB]), oacc[j % DB]);
+                if constexpr (NEXT) {
+                    if constexpr (j == 2) alpha = move_max(tile_max(sn, kbyte[nb], (T + 1) * BN, false));
+                    if constexpr (j >= 3 && j < 7) exp_pair(sn, 0, j - 3, pk0n);
+                }
+            }
+            if constexpr (s >= NSS - LT && s - (NSS - LT) < NPV) v_read(vb, s - (NSS - LT), trv[s - (NSS - LT)]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if constexpr (NEXT) {
+            if (moved) rescale_out(alpha);
+            sc[0] = sn[0];
+            sc[1] = sn[1];
+            pk[0] = pk0n;
+        }
+        if (T + 1 < ntiles) wait_vmem();
         __syncthreads();
     };
-    for (int it = 0; it < ntiles; it += 2) {
-        tile(it, std::integral_constant<int, 0>{});
-        if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
+    {
+        int T = 0;
+        for (; T + 2 < nfull; T += 2) {
+            iteration(T, B0{}, std::true_type{});
+            iteration(T + 1, B1{}, std::true_type{});
+        }
+        if (T + 1 < nfull) {
+            iteration(T, B0{}, std::true_type{});
+            iteration(T + 1, B1{}, std::false_type{});
+        } else if (T < nfull) {
+            iteration(T, B0{}, std::false_type{});
+        }
+    }
+    if (nfull < ntiles) {
+        // the partial last tile (keys past the chunk read as zero and are masked)
+        const int T = nfull;
+        const RA_LDS char* kb = lbase + (2 * (T & 1)) * TILEB;
+        const RA_LDS char* vb = lbase + (2 * (T & 1) + 1) * TILEB;
+        s_tile(kb, sc);
+        const float alpha = move_max(tile_max(sc, kbyte[T & 1], T * BN, true));
+        if (moved) rescale_out(alpha);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) exp_pair(sc, t, j, pk[t]);
+        pv_tile(vb, pk);
     }
 
     l = half_sum(l);

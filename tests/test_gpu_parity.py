@@ -445,3 +445,45 @@ def test_gpu_refusals_raise():
         ra.ring_fwd(q, k, k, ra.Chunks([8]))
     with pytest.raises(ValueError):
         ra.ring_fwd(q.cpu(), k.cpu(), k.cpu(), ra.Chunks([8]))
+
+
+# ------------------------------------------------------------------ forward tile counts
+# Chunk lengths around the 64-key tile edges: no full tile, one, two, three, five full
+# tiles, with and without a partial last tile.  The forward pipelines the full tiles
+# (scores of tile T + 1 overlap P and P V of tile T) and runs a partial tile after the
+# loop, so each count takes a different path through that control flow.
+TILE_EDGE_KEYS = (1, 63, 64, 65, 128, 129, 192, 193, 320, 333)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("masked", [False, True], ids=["dense", "masked"])
+def test_forward_at_tile_edges(D, masked):
+    B, Sq, Hq, Hkv = 2, 70, 4, 2
+    for n, Sk in enumerate(TILE_EDGE_KEYS):
+        seed = 1200 + 10 * n + D
+        S = Sk + 64  # the sweep: this chunk, then a full 64-key chunk merged into it
+        q = W.randn((B, Sq, Hq, D), seed, "bf16")
+        k = W.randn((B, S, Hkv, D), seed + 1, "bf16")
+        v = W.randn((B, S, Hkv, D), seed + 2, "bf16")
+        m = W.make_key_mask(B, S, seed + 3, p_keep=0.7, masked_ranges=[(1, 0, min(Sk, 130))]) if masked else None
+        gq, gk, gv = to_dev(q, k, v)
+        gm = m.to(dev()) if masked else None
+        for lens, order in (((Sk,), (0,)), ((Sk, 64), (1, 0))):
+            if len(lens) == 1:
+                kk, vv, mm = gk[:, :Sk], gv[:, :Sk], (gm[:, :Sk] if masked else None)
+            else:
+                kk, vv, mm = gk, gv, gm
+            out, lse = ra.ring_fwd(gq, kk, vv, ra.Chunks(list(lens), list(order)), out_dtype=torch.float32, kmask=mm)
+            torch.cuda.synchronize()
+            kn, vn = np64(kk.cpu()), np64(vv.cpu())
+            mn = mm.cpu().numpy().astype(np.uint8) if masked else None
+            ref_o, ref_l = oracle.attention_forward(np64(q), kn, vn, kmask=mn)
+            o, l = np64(out), np64(lse)
+            assert not np.isnan(o).any(), (Sk, lens)
+            assert np.array_equal(np.isneginf(l), np.isneginf(ref_l)), (Sk, lens)
+            fin = np.isfinite(ref_l)
+            if fin.any():
+                assert max_abs(l[fin], ref_l[fin]) <= LSE_TOL_BF16, (Sk, lens)
+            if np.any(ref_o != 0):
+                assert rel(o, ref_o) <= BF16_TOL, (Sk, lens, rel(o, ref_o))
+            assert np.all(o[np.broadcast_to(~fin.transpose(0, 2, 1)[..., None], o.shape)] == 0), (Sk, lens)

@@ -197,8 +197,14 @@ __device__ __forceinline__ void dma16(i32x4_t desc, RA_LDS void* dst, uint32_t v
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(desc)
                  : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read exactly once (it should not
+// displace reused tiles from the caches).
+__device__ __forceinline__ void dma16_once(i32x4_t desc, RA_LDS void* dst, uint32_t voff) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds" ::"s"(m0v), "v"(voff), "s"(desc)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
-
 // s_waitcnt vmcnt(0): this wavefront's buffer loads (incl. the LDS copies) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -1113,7 +1119,7 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
         const int64_t off = ((int64_t)it * p.ds_nqt + qt) * 4096;
         const i32x4_t rd = make_desc(slab + off, off < slab_bytes ? (uint32_t)(slab_bytes - off) : 0u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(rd, st + KTB + w * 4096 + i * 1024, vds[i]);
+        for (int i = 0; i < 4; ++i) dma16_once(rd, st + KTB + w * 4096 + i * 1024, vds[i]);
     };
     // lane-constant LDS offsets: K^T reads (as V^T in the forward) and dS^T reads
     const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);

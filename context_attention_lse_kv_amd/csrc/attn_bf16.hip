@@ -425,6 +425,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         }
         static_for<0, NSS + NPV>([&](auto sc_) {
             constexpr int s = decltype(sc_)::value;
+            // raised wave priority over the slots that mix MFMAs with softmax work: the
+            // other workgroup's wavefront on the SIMD then fills the gaps with its own
+            // MFMAs rather than taking the issue slots first
+            if constexpr (s == 0) __builtin_amdgcn_s_setprio(1);
+            if constexpr (s == NSS + 7) __builtin_amdgcn_s_setprio(0);
             if constexpr (s < NSS) {
                 if constexpr (NEXT) {
                     sn[s / KS] = mfma32(stk[s], qreg[s % KS], s % KS == 0 ? f32x16_t{} : sn[s / KS]);
@@ -778,6 +783,9 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
             for (int i = 0; i < PF; ++i) row_read(i);
 #pragma unroll
             for (int i = 0; i < LT; ++i) tr_read(i);
+            // raised priority while this wavefront issues MFMAs, so that its partner on the
+            // SIMD (the other role, in its softmax burst) yields the issue slots to them
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int s = 0; s < NSLOT; ++s) {
                 const int rb = s / KS, ks = s % KS, grp = s / DB, db = s % DB;
@@ -788,6 +796,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                 if (s + LT < NSLOT) tr_read(s + LT);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
 
         if (role == 0) {

@@ -389,10 +389,32 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     // scheduling barrier closes each slot.  K tile T + 2 and V tile T + 1 are copied
     // during iteration T (one barrier per iteration).  A partial last tile runs after
     // the loop without pipelining.
-    const int nfull = p.Sk / BN, ntiles = (p.Sk + BN - 1) / BN;
+    const int ntiles_all = (p.Sk + BN - 1) / BN;
     issue_k(0, B0{});
     issue_v(0, B0{});
-    if (ntiles > 1) issue_k(1, B1{});
+    if (ntiles_all > 1) issue_k(1, B1{});
+    // With the key mask, the sweep ends at the last tile that holds a valid key: the tiles
+    // after it (right padding) would add exactly nothing.  Each wavefront scans every
+    // fourth tile from the end, four tiles per round, and stops at its first valid key;
+    // the highest hit of the four wavefronts bounds the sweep.
+    int sk_eff = p.Sk;
+    if constexpr (MASK) {
+        __shared__ int last_valid[4];
+        int last = -1;
+        for (int t0 = ntiles_all - 1 - w; t0 >= 0 && last < 0; t0 -= 16) {
+            uint32_t kb4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kb4[j] = t0 - 4 * j >= 0 ? load_key_byte(km_b, p.Sk, (t0 - 4 * j) * BN, lane) : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (last < 0 && __builtin_amdgcn_ballot_w64(kb4[j] != 0) != 0) last = t0 - 4 * j;
+        }
+        if (lane == 0) last_valid[w] = last;
+        __syncthreads();
+        const int lv = max(max(last_valid[0], last_valid[1]), max(last_valid[2], last_valid[3]));
+        sk_eff = min(p.Sk, (lv + 1) * BN);
+    }
+    const int nfull = sk_eff / BN, ntiles = (sk_eff + BN - 1) / BN;
     wait_vmem();
     __syncthreads();
     f32x16_t sc[2];   // scores of the tile whose P is being formed

@@ -451,7 +451,8 @@ def test_gpu_refusals_raise():
 # Chunk lengths around the 64-key tile edges: no full tile, one, two, three, five full
 # tiles, with and without a partial last tile.  The forward pipelines the full tiles
 # (scores of tile T + 1 overlap P and P V of tile T) and runs a partial tile after the
-# loop, so each count takes a different path through that control flow.
+# loop, so each count takes a different path through that control flow.  With the key
+# mask, a sweep also ends early at the last tile that holds a valid key.
 TILE_EDGE_KEYS = (1, 63, 64, 65, 128, 129, 192, 193, 320, 333)
 
 
@@ -465,7 +466,10 @@ def test_forward_at_tile_edges(D, masked):
         q = W.randn((B, Sq, Hq, D), seed, "bf16")
         k = W.randn((B, S, Hkv, D), seed + 1, "bf16")
         v = W.randn((B, S, Hkv, D), seed + 2, "bf16")
-        m = W.make_key_mask(B, S, seed + 3, p_keep=0.7, masked_ranges=[(1, 0, min(Sk, 130))]) if masked else None
+        # batch 0: keys from Sk - 70 on masked (whole tiles at the end of the chunk with
+        # no valid key); batch 1: the first keys masked
+        m = (W.make_key_mask(B, S, seed + 3, p_keep=0.7, valid_len=(max(1, Sk - 70), S),
+                             masked_ranges=[(1, 0, min(Sk, 130))]) if masked else None)
         gq, gk, gv = to_dev(q, k, v)
         gm = m.to(dev()) if masked else None
         for lens, order in (((Sk,), (0,)), ((Sk, 64), (1, 0))):

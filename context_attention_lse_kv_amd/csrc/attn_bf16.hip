@@ -1182,7 +1182,33 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qr][db] = f32x16_t{};
 
-    const int ntiles = (p.Sk + BN - 1) / BN;
+    int ntiles = (p.Sk + BN - 1) / BN;
+    if (p.km != nullptr) {
+        // dS of the keys after the last valid key of the chunk is zero: the key loop ends at
+        // the 64-key tile that holds that key (each wavefront scans every kDqsWaves-th tile
+        // from the end; the highest hit bounds the loop).  Two words of LDS per wavefront
+        // carry the hits, before any tile copy lands there.
+        const uint8_t* km_b = p.km + (int64_t)b * p.km_sB;
+        const int nt64 = (p.Sk + 63) / 64;
+        int last = -1;
+        for (int t0 = nt64 - 1 - w; t0 >= 0 && last < 0; t0 -= 4 * kDqsWaves) {
+            uint32_t kb4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kb4[j] = t0 - kDqsWaves * j >= 0 ? load_key_byte(km_b, p.Sk, (t0 - kDqsWaves * j) * 64, lane) : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (last < 0 && __builtin_amdgcn_ballot_w64(kb4[j] != 0) != 0) last = t0 - kDqsWaves * j;
+        }
+        RA_LDS int* const hits = (RA_LDS int*)lbase;
+        if (lane == 0) hits[w] = last;
+        __syncthreads();
+        int lv = -1;
+#pragma unroll
+        for (int i = 0; i < kDqsWaves; ++i) lv = max(lv, hits[i]);
+        __syncthreads();
+        ntiles = (min(p.Sk, (lv + 1) * 64) + BN - 1) / BN;
+    }
 #pragma unroll
     for (int i = 0; i < kDqsStages - 1; ++i)
         if (i < ntiles) issue(i);
@@ -1383,9 +1409,14 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
 }
 
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
-                               const ra_tensor& dq_acc, hipStream_t s, bool dq_read, const ra_tensor* dq_out) {
+                               const ra_tensor& dq_acc, hipStream_t s, bool dq_read, const ra_tensor* dq_out,
+                               const KeyMask* km) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, k, q, ra_lse{}, ra_lse{}, scale);
+    if (km) {
+        p.km = km->data;
+        p.km_sB = km->sB;
+    }
     p.dq = (float*)dq_acc.data;
     p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
     p.dq_read = dq_read ? 1 : 0;

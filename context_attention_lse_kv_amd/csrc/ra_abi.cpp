@@ -633,7 +633,8 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
             RA_HIP(ra::launch_bwd_dkdv_bf16(qs, kc, vc, dos, ls, dls, km, scale, dkc, dvc, ds, s,
                                             direct_kv ? &dko : nullptr, direct_kv ? &dvo : nullptr));
             RA_HIP(ra::launch_bwd_dqs_bf16(qs, kc, ds, scale, dqs, s, !(direct_dq && i == 0),
-                                           direct_dq && i + 1 == steps.size() ? &dqo : nullptr));
+                                           direct_dq && i + 1 == steps.size() ? &dqo : nullptr,
+                                           km.data ? &km : nullptr));
         }
     }
     if (dq->dtype == RA_BF16 && !direct_dq) RA_HIP(ra::launch_cast_f32_to_bf16(dq_acc, *dq, s));

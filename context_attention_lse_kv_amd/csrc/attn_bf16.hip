@@ -8,20 +8,24 @@
 // state (running max m, running sum l) and the rescale of the output are
 // lane-local, and the probabilities P^T come out of the MFMA already in the
 // operand layout of the second product O^T += V^T P^T.  V stays row-major in LDS;
-// its transposed operand is read with the gfx950 transposing LDS read.  The
+// its transposed operand is read with the gfx950 transposing LDS read.  The key
+// tiles run as a software pipeline one tile deep (the scores of tile T + 1 are
+// formed while P of tile T is exponentiated and P V of tile T accumulates).  The
 // running max is only moved when a row's maximum grows by more than kRescale
 // (base-2 units), so the output rescale is skipped on almost every tile.  The
 // epilogue either writes the step's partial (normalised output, LSE) or merges it
 // into the running fp32 (output, LSE) by LSE rescaling (the merge of the
 // diffusers issue "Ring attention backward uses stale iteration-0 KV", table "How
-// it surfaces per backend": ring needs LSE for partial-result merging).
+// it surfaces per backend": ring needs LSE for partial-result merging); the last
+// step of a bf16 sweep writes the merged output in bf16.
 //
 // Backward (one chunk step against that step's own K/V chunk - the point of that
 // issue's "Root cause" and "Expected behavior") runs as two kernels with no atomics.
 // The KV-stationary kernel owns 128 keys of the chunk for one KV head and sweeps the
 // query rows of every query head of that GQA group in LDS tiles of 64; each 32-key
 // group has two wavefronts in split roles (S, P, dV and dP, dS, dK) running one Q
-// tile apart, and the workgroup adds its dK/dV rows with plain read-modify-writes.
+// tile apart, and the workgroup adds its dK/dV rows with plain read-modify-writes
+// (or, when the launch is the only one for the chunk, writes them in bf16).
 // dQ takes one of two routes, both free of atomics (adding dQ from every key tile
 // through device-scope atomics costs more on this chip than either).  Stored dS: the
 // KV-stationary kernel also writes the dS it holds (bf16) to a caller buffer, and a

@@ -225,10 +225,10 @@ __device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
 
 // ============================================================================ forward
 template <int D, bool MERGE, bool MASK>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void fwd_bf16_kernel(FwdParams p) {
     constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
     constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
-    constexpr int RPI = 1024 / ROWB, NI = BN / RPI / 4;
+    constexpr int RPI = 1024 / ROWB, NI = BN / RPI / kFwdWaves;
     constexpr int NSS = 2 * KS, NPV = 4 * DB;  // S^T and P V MFMAs per tile
     static_assert(RC >= 8 && NI >= 1, "tile geometry");
     __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [K0 | V0 | K1 | V1]
@@ -399,23 +399,26 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     if (ntiles_all > 1) issue_k(1, B1{});
     // With the key mask, the sweep ends at the last tile that holds a valid key: the tiles
     // after it (right padding) would add exactly nothing.  Each wavefront scans every
-    // fourth tile from the end, four tiles per round, and stops at its first valid key;
-    // the highest hit of the four wavefronts bounds the sweep.
+    // kFwdWaves-th tile from the end, four tiles per round, and stops at its first valid
+    // key; the highest hit of the workgroup's wavefronts bounds the sweep.
     int sk_eff = p.Sk;
     if constexpr (MASK) {
-        __shared__ int last_valid[4];
+        __shared__ int last_valid[kFwdWaves];
         int last = -1;
-        for (int t0 = ntiles_all - 1 - w; t0 >= 0 && last < 0; t0 -= 16) {
+        for (int t0 = ntiles_all - 1 - w; t0 >= 0 && last < 0; t0 -= 4 * kFwdWaves) {
             uint32_t kb4[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) kb4[j] = t0 - 4 * j >= 0 ? load_key_byte(km_b, p.Sk, (t0 - 4 * j) * BN, lane) : 0u;
+            for (int j = 0; j < 4; ++j)
+                kb4[j] = t0 - kFwdWaves * j >= 0 ? load_key_byte(km_b, p.Sk, (t0 - kFwdWaves * j) * BN, lane) : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (last < 0 && __builtin_amdgcn_ballot_w64(kb4[j] != 0) != 0) last = t0 - 4 * j;
+                if (last < 0 && __builtin_amdgcn_ballot_w64(kb4[j] != 0) != 0) last = t0 - kFwdWaves * j;
         }
         if (lane == 0) last_valid[w] = last;
         __syncthreads();
-        const int lv = max(max(last_valid[0], last_valid[1]), max(last_valid[2], last_valid[3]));
+        int lv = -1;
+#pragma unroll
+        for (int i = 0; i < kFwdWaves; ++i) lv = max(lv, last_valid[i]);
         sk_eff = min(p.Sk, (lv + 1) * BN);
     }
     const int nfull = sk_eff / BN, ntiles = (sk_eff + BN - 1) / BN;
@@ -1315,11 +1318,11 @@ hipError_t launch_fwd_chunk_bf16(const ra_tensor& q, const ra_tensor& k, const r
     p.o16_sH = out16 ? out16->sH : 0;
     const bool mk = km.data != nullptr;
     if (q.D == 64) {
-        if (merge) mk ? fwd_bf16_kernel<64, true, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<64, true, false><<<nb, 256, 0, s>>>(p);
-        else mk ? fwd_bf16_kernel<64, false, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<64, false, false><<<nb, 256, 0, s>>>(p);
+        if (merge) mk ? fwd_bf16_kernel<64, true, true><<<nb, 64 * kFwdWaves, 0, s>>>(p) : fwd_bf16_kernel<64, true, false><<<nb, 64 * kFwdWaves, 0, s>>>(p);
+        else mk ? fwd_bf16_kernel<64, false, true><<<nb, 64 * kFwdWaves, 0, s>>>(p) : fwd_bf16_kernel<64, false, false><<<nb, 64 * kFwdWaves, 0, s>>>(p);
     } else {
-        if (merge) mk ? fwd_bf16_kernel<128, true, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<128, true, false><<<nb, 256, 0, s>>>(p);
-        else mk ? fwd_bf16_kernel<128, false, true><<<nb, 256, 0, s>>>(p) : fwd_bf16_kernel<128, false, false><<<nb, 256, 0, s>>>(p);
+        if (merge) mk ? fwd_bf16_kernel<128, true, true><<<nb, 64 * kFwdWaves, 0, s>>>(p) : fwd_bf16_kernel<128, true, false><<<nb, 64 * kFwdWaves, 0, s>>>(p);
+        else mk ? fwd_bf16_kernel<128, false, true><<<nb, 64 * kFwdWaves, 0, s>>>(p) : fwd_bf16_kernel<128, false, false><<<nb, 64 * kFwdWaves, 0, s>>>(p);
     }
     return hipGetLastError();
 }

@@ -225,7 +225,7 @@ __device__ __forceinline__ uint32_t copy_voff(int ci, int lane, int64_t sS) {
 
 // ============================================================================ forward
 template <int D, bool MERGE, bool MASK>
-__global__ __launch_bounds__(64 * kFwdWaves, 8 / kFwdWaves) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p) {  // 2 wavefronts per SIMD
     constexpr int KS = D / 16, DB = D / 32, BN = kFwdBlockN, BM = kFwdBlockM;
     constexpr int RC = D / 8, ROWB = D * 2, TILEB = BN * ROWB;
     constexpr int RPI = 1024 / ROWB, NI = BN / RPI / kFwdWaves;

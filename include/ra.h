@@ -219,7 +219,9 @@ ra_status ra_bwd_chunk_dq_ds(const ra_tensor* q, const ra_tensor* k, const void*
  * result is written to out (bf16 or fp32) and lse.  k, v hold the whole key
  * sequence [B,S_k,H_kv,D]; chunks tile it.  ws: device workspace of at least
  * ra_ring_fwd_workspace_bytes(q, out) bytes (fp32 running output when out is
- * bf16; 0 bytes needed when out is fp32). */
+ * bf16; 0 bytes needed when out is fp32).  With bf16 inputs and a bf16 out, the
+ * last non-empty step writes the merged output to out directly, rounded to
+ * nearest even: the same values as rounding the fp32 running output. */
 ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
                       const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse,
                       void* ws, size_t ws_bytes, void* stream);

@@ -101,6 +101,14 @@ struct BwdParams {
     // query tile), ds_nkg groups x ds_nqt tiles per (batch, query head); null = none
     uint16_t* ds;
     int ds_nqt, ds_nkg;
+    // dQ pass over two chunks at once (one read and write of the dQ accumulator for both):
+    // the second chunk's keys (rows of the same k tensor), length, dS blocks and key mask,
+    // or ds2 = null
+    const uint16_t* k2;
+    uint32_t k2_bytes;
+    int Sk2, ds_nkg2;
+    uint16_t* ds2;
+    const uint8_t* km2;
     // Final bf16 outputs written once instead of the fp32 accumulators (dK/dV of a chunk
     // swept in one launch; dQ of the last chunk of a sweep), or null.  dq_read = 0: the
     // dQ pass treats the fp32 accumulator as zero (first chunk of a sweep) and stores.
@@ -1136,26 +1144,39 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
     const int qt = qb * kDqsWaves + w;  // this wavefront's 64-row query tile
     const bool copies_k = w < KCOPIES;   // uniform per wavefront
 
-    // this wavefront's dS blocks (key group it, tile qt) at (it ds_nqt + qt) of the (batch,
+    // this wavefront's dS blocks (key group t, tile qt) at (t ds_nqt + qt) of the (batch,
     // head) slab, so that a workgroup's wavefronts read adjacent blocks.  A tile at or past
     // ds_nqt (rows past the end, never stored) reads another group's block or, past the
-    // slab, zeros.
-    const int64_t slab_blocks = (int64_t)p.ds_nqt * p.ds_nkg;
-    const char* slab = (const char*)p.ds + ((int64_t)b * p.Hq + h) * slab_blocks * 4096;
-    const int64_t slab_bytes = slab_blocks * 4096;
+    // slab, zeros.  With a second chunk, its key tiles follow the first chunk's.
+    struct Chunk {
+        const char* slab;
+        int64_t slab_bytes;
+        const uint16_t* kbase;
+        uint32_t kbytes;
+    };
+    auto chunk_of = [&](const uint16_t* ds, int nkg, const uint16_t* k, uint32_t kbytes) {
+        const int64_t slab_blocks = (int64_t)p.ds_nqt * nkg;
+        return Chunk{(const char*)ds + ((int64_t)b * p.Hq + h) * slab_blocks * 4096, slab_blocks * 4096,
+                     k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH, kbytes};
+    };
+    const Chunk ca = chunk_of(p.ds, p.ds_nkg, p.k, p.k_bytes);
+    const Chunk cb = p.ds2 ? chunk_of(p.ds2, p.ds_nkg2, p.k2, p.k2_bytes) : ca;
     uint32_t vds[4];  // copy offsets: LDS chunk 64 i + lane <- block chunk (64 i + lane) ^ 8 (i & 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) vds[i] = (uint32_t)(((64 * i + lane) ^ (8 * (i & 1))) * 16);
 
-    const uint16_t* kbase = p.k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH;
     const uint32_t vk = copy_voff<D>(w, lane, p.k_sS);
-    // tile it (keys 32 it ..) into stage it % kDqsStages: one K copy (first KCOPIES
-    // wavefronts) and the wavefront's own dS block
+    int nta = 0;  // key tiles of the first chunk (the second chunk's follow)
+    // tile it (keys 32 t .. of its chunk) into stage it % kDqsStages: one K copy (first
+    // KCOPIES wavefronts) and the wavefront's own dS block
     auto issue = [&](int it) {
         RA_LDS char* st = lbase + (it % kDqsStages) * STB;
-        if (copies_k) dma16(tile_desc(kbase, (int64_t)it * BN, p.k_sS * 2, p.k_bytes), st + w * 1024, vk);
-        const int64_t off = ((int64_t)it * p.ds_nqt + qt) * 4096;
-        const i32x4_t rd = make_desc(slab + off, off < slab_bytes ? (uint32_t)(slab_bytes - off) : 0u);
+        const bool second = it >= nta;
+        const Chunk& c = second ? cb : ca;
+        const int t = second ? it - nta : it;
+        if (copies_k) dma16(tile_desc(c.kbase, (int64_t)t * BN, p.k_sS * 2, c.kbytes), st + w * 1024, vk);
+        const int64_t off = ((int64_t)t * p.ds_nqt + qt) * 4096;
+        const i32x4_t rd = make_desc(c.slab + off, off < c.slab_bytes ? (uint32_t)(c.slab_bytes - off) : 0u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_once(rd, st + KTB + w * 4096 + i * 1024, vds[i]);
     };
@@ -1189,20 +1210,20 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[qr][db] = f32x16_t{};
 
-    int ntiles = (p.Sk + BN - 1) / BN;
-    if (p.km != nullptr) {
-        // dS of the keys after the last valid key of the chunk is zero: the key loop ends at
-        // the 64-key tile that holds that key (each wavefront scans every kDqsWaves-th tile
-        // from the end; the highest hit bounds the loop).  Two words of LDS per wavefront
-        // carry the hits, before any tile copy lands there.
-        const uint8_t* km_b = p.km + (int64_t)b * p.km_sB;
-        const int nt64 = (p.Sk + 63) / 64;
+    // Key tiles of a chunk.  With its key mask: dS of the keys after the last valid key is
+    // zero, so the tiles end at the 64-key tile that holds that key (each wavefront scans
+    // every kDqsWaves-th tile from the end; the highest hit bounds the loop).  One word of
+    // LDS per wavefront carries the hits, before any tile copy lands there.
+    auto key_tiles = [&](const uint8_t* km, int Sk) {
+        if (km == nullptr) return (Sk + BN - 1) / BN;
+        const uint8_t* km_b = km + (int64_t)b * p.km_sB;
+        const int nt64 = (Sk + 63) / 64;
         int last = -1;
         for (int t0 = nt64 - 1 - w; t0 >= 0 && last < 0; t0 -= 4 * kDqsWaves) {
             uint32_t kb4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                kb4[j] = t0 - kDqsWaves * j >= 0 ? load_key_byte(km_b, p.Sk, (t0 - kDqsWaves * j) * 64, lane) : 0u;
+                kb4[j] = t0 - kDqsWaves * j >= 0 ? load_key_byte(km_b, Sk, (t0 - kDqsWaves * j) * 64, lane) : 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (last < 0 && __builtin_amdgcn_ballot_w64(kb4[j] != 0) != 0) last = t0 - kDqsWaves * j;
@@ -1214,8 +1235,10 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
 #pragma unroll
         for (int i = 0; i < kDqsWaves; ++i) lv = max(lv, hits[i]);
         __syncthreads();
-        ntiles = (min(p.Sk, (lv + 1) * 64) + BN - 1) / BN;
-    }
+        return (min(Sk, (lv + 1) * 64) + BN - 1) / BN;
+    };
+    nta = key_tiles(p.km, p.Sk);
+    const int ntiles = nta + (p.ds2 ? key_tiles(p.km2, p.Sk2) : 0);
 #pragma unroll
     for (int i = 0; i < kDqsStages - 1; ++i)
         if (i < ntiles) issue(i);
@@ -1356,6 +1379,12 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
     p.km = nullptr;
     p.km_sB = 0;
     p.ds = nullptr;
+    p.k2 = nullptr;
+    p.k2_bytes = 0;
+    p.Sk2 = 0;
+    p.ds_nkg2 = 0;
+    p.ds2 = nullptr;
+    p.km2 = nullptr;
     p.ds_nqt = p.ds_nkg = 0;
     p.dk16 = p.dv16 = p.dq16 = nullptr;
     p.dk16_sB = p.dk16_sS = p.dk16_sH = p.dv16_sB = p.dv16_sS = p.dv16_sH = p.dq16_sB = p.dq16_sS = p.dq16_sH = 0;
@@ -1417,12 +1446,20 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
 
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
                                const ra_tensor& dq_acc, hipStream_t s, bool dq_read, const ra_tensor* dq_out,
-                               const KeyMask* km) {
+                               const KeyMask* km, const DqsChunk* second) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, k, q, ra_lse{}, ra_lse{}, scale);
     if (km) {
         p.km = km->data;
         p.km_sB = km->sB;
+    }
+    if (second && second->k.S > 0) {
+        p.k2 = (const uint16_t*)second->k.data;
+        p.k2_bytes = span_bytes(second->k.S, second->k.sS, second->k.D);
+        p.Sk2 = second->k.S;
+        p.ds_nkg2 = ds_key_groups(second->k.S);
+        p.ds2 = (uint16_t*)second->ds;
+        p.km2 = second->km ? second->km->data : nullptr;
     }
     p.dq = (float*)dq_acc.data;
     p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;

@@ -625,6 +625,32 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
         // bf16: the dK/dV kernel stores dS, the dQ pass reads it back (no second S, dP)
         const ra_tensor dko = seq_slice(*dk, chunks->start[c], chunks->len[c]);
         const ra_tensor dvo = seq_slice(*dv, chunks->start[c], chunks->len[c]);
+        if (single && i + 1 < steps.size()) {
+            // Two chunks per dQ pass when both dS fit the region (the second after the
+            // first): the dQ accumulator is then read and written once per pair of chunks.
+            const int c2 = steps[i + 1].c;
+            const int64_t off2 = (int64_t)round256((size_t)ra::ds_bytes(q->B, q->H, q->S, chunks->len[c]));
+            if (off2 + ra::ds_bytes(q->B, q->H, q->S, chunks->len[c2]) <= ds_room) {
+                void* const ds2 = (char*)ds + off2;
+                const ra_tensor kc2 = seq_slice(*k, chunks->start[c2], chunks->len[c2]);
+                const ra_tensor vc2 = seq_slice(*v, chunks->start[c2], chunks->len[c2]);
+                const ra_tensor dkc2 = seq_slice(dk_acc, chunks->start[c2], chunks->len[c2]);
+                const ra_tensor dvc2 = seq_slice(dv_acc, chunks->start[c2], chunks->len[c2]);
+                const ra_tensor dko2 = seq_slice(*dk, chunks->start[c2], chunks->len[c2]);
+                const ra_tensor dvo2 = seq_slice(*dv, chunks->start[c2], chunks->len[c2]);
+                const ra::KeyMask km2 = key_mask(kmask, chunks->start[c2]);
+                RA_HIP(ra::launch_bwd_dkdv_bf16(*q, kc, vc, *dout, *lse, delta, km, scale, dkc, dvc, ds, s,
+                                                direct_kv ? &dko : nullptr, direct_kv ? &dvo : nullptr));
+                RA_HIP(ra::launch_bwd_dkdv_bf16(*q, kc2, vc2, *dout, *lse, delta, km2, scale, dkc2, dvc2, ds2, s,
+                                                direct_kv ? &dko2 : nullptr, direct_kv ? &dvo2 : nullptr));
+                const ra::DqsChunk second{kc2, ds2, km2.data ? &km2 : nullptr};
+                RA_HIP(ra::launch_bwd_dqs_bf16(*q, kc, ds, scale, dq_acc, s, !(direct_dq && i == 0),
+                                               direct_dq && i + 2 == steps.size() ? dq : nullptr,
+                                               km.data ? &km : nullptr, &second));
+                ++i;
+                continue;
+            }
+        }
         for (int32_t r0 = 0; r0 < q->S; r0 += rows) {
             const int32_t n = std::min(rows, q->S - r0);
             const ra_tensor qs = seq_slice(*q, r0, n), dos = seq_slice(*dout, r0, n), dqs = seq_slice(dq_acc, r0, n);

@@ -101,14 +101,15 @@ struct BwdParams {
     // query tile), ds_nkg groups x ds_nqt tiles per (batch, query head); null = none
     uint16_t* ds;
     int ds_nqt, ds_nkg;
-    // dQ pass over two chunks at once (one read and write of the dQ accumulator for both):
-    // the second chunk's keys (rows of the same k tensor), length, dS blocks and key mask,
-    // or ds2 = null
-    const uint16_t* k2;
-    uint32_t k2_bytes;
-    int Sk2, ds_nkg2;
-    uint16_t* ds2;
-    const uint8_t* km2;
+    // dQ pass over several chunks at once (one read and write of the dQ accumulator for
+    // all of them): chunk j's keys (rows of the same k tensor), length, dS blocks and key
+    // mask, for j < n_dqs
+    int n_dqs;
+    const uint16_t* dqs_k[kDqsMaxChunks];
+    uint32_t dqs_kbytes[kDqsMaxChunks];
+    int dqs_Sk[kDqsMaxChunks], dqs_nkg[kDqsMaxChunks];
+    const uint16_t* dqs_ds[kDqsMaxChunks];
+    const uint8_t* dqs_km[kDqsMaxChunks];
     // Final bf16 outputs written once instead of the fp32 accumulators (dK/dV of a chunk
     // swept in one launch; dQ of the last chunk of a sweep), or null.  dq_read = 0: the
     // dQ pass treats the fp32 accumulator as zero (first chunk of a sweep) and stores.
@@ -1154,26 +1155,29 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
         const uint16_t* kbase;
         uint32_t kbytes;
     };
-    auto chunk_of = [&](const uint16_t* ds, int nkg, const uint16_t* k, uint32_t kbytes) {
-        const int64_t slab_blocks = (int64_t)p.ds_nqt * nkg;
-        return Chunk{(const char*)ds + ((int64_t)b * p.Hq + h) * slab_blocks * 4096, slab_blocks * 4096,
-                     k + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH, kbytes};
+    auto chunk_of = [&](int j) {
+        const int64_t slab_blocks = (int64_t)p.ds_nqt * p.dqs_nkg[j];
+        return Chunk{(const char*)p.dqs_ds[j] + ((int64_t)b * p.Hq + h) * slab_blocks * 4096, slab_blocks * 4096,
+                     p.dqs_k[j] + (int64_t)b * p.k_sB + (int64_t)g * p.k_sH, p.dqs_kbytes[j]};
     };
-    const Chunk ca = chunk_of(p.ds, p.ds_nkg, p.k, p.k_bytes);
-    const Chunk cb = p.ds2 ? chunk_of(p.ds2, p.ds_nkg2, p.k2, p.k2_bytes) : ca;
     uint32_t vds[4];  // copy offsets: LDS chunk 64 i + lane <- block chunk (64 i + lane) ^ 8 (i & 1)
 #pragma unroll
     for (int i = 0; i < 4; ++i) vds[i] = (uint32_t)(((64 * i + lane) ^ (8 * (i & 1))) * 16);
 
     const uint32_t vk = copy_voff<D>(w, lane, p.k_sS);
-    int nta = 0;  // key tiles of the first chunk (the second chunk's follow)
+    int first[kDqsMaxChunks];  // first key tile of each chunk in the pass's tile order
     // tile it (keys 32 t .. of its chunk) into stage it % kDqsStages: one K copy (first
     // KCOPIES wavefronts) and the wavefront's own dS block
     auto issue = [&](int it) {
         RA_LDS char* st = lbase + (it % kDqsStages) * STB;
-        const bool second = it >= nta;
-        const Chunk& c = second ? cb : ca;
-        const int t = second ? it - nta : it;
+        int j = 0, t = it;  // chunk of tile it and the tile's index within it
+#pragma unroll
+        for (int jj = 1; jj < kDqsMaxChunks; ++jj)
+            if (jj < p.n_dqs && it >= first[jj]) {
+                j = jj;
+                t = it - first[jj];
+            }
+        const Chunk c = chunk_of(j);
         if (copies_k) dma16(tile_desc(c.kbase, (int64_t)t * BN, p.k_sS * 2, c.kbytes), st + w * 1024, vk);
         const int64_t off = ((int64_t)t * p.ds_nqt + qt) * 4096;
         const i32x4_t rd = make_desc(c.slab + off, off < c.slab_bytes ? (uint32_t)(c.slab_bytes - off) : 0u);
@@ -1237,8 +1241,12 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
         __syncthreads();
         return (min(Sk, (lv + 1) * 64) + BN - 1) / BN;
     };
-    nta = key_tiles(p.km, p.Sk);
-    const int ntiles = nta + (p.ds2 ? key_tiles(p.km2, p.Sk2) : 0);
+    int ntiles = 0;
+#pragma unroll
+    for (int j = 0; j < kDqsMaxChunks; ++j) {
+        first[j] = ntiles;
+        if (j < p.n_dqs) ntiles += key_tiles(p.dqs_km[j], p.dqs_Sk[j]);
+    }
 #pragma unroll
     for (int i = 0; i < kDqsStages - 1; ++i)
         if (i < ntiles) issue(i);
@@ -1379,12 +1387,7 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
     p.km = nullptr;
     p.km_sB = 0;
     p.ds = nullptr;
-    p.k2 = nullptr;
-    p.k2_bytes = 0;
-    p.Sk2 = 0;
-    p.ds_nkg2 = 0;
-    p.ds2 = nullptr;
-    p.km2 = nullptr;
+    p.n_dqs = 0;
     p.ds_nqt = p.ds_nkg = 0;
     p.dk16 = p.dv16 = p.dq16 = nullptr;
     p.dk16_sB = p.dk16_sS = p.dk16_sH = p.dv16_sB = p.dv16_sS = p.dv16_sH = p.dq16_sB = p.dq16_sS = p.dq16_sH = 0;
@@ -1446,21 +1449,25 @@ hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_t
 
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
                                const ra_tensor& dq_acc, hipStream_t s, bool dq_read, const ra_tensor* dq_out,
-                               const KeyMask* km, const DqsChunk* second) {
+                               const KeyMask* km, const DqsChunk* more, int n_more) {
     if (q.S == 0 || k.S == 0) return hipSuccess;
     BwdParams p = bwd_params(q, k, k, q, ra_lse{}, ra_lse{}, scale);
     if (km) {
         p.km = km->data;
         p.km_sB = km->sB;
     }
-    if (second && second->k.S > 0) {
-        p.k2 = (const uint16_t*)second->k.data;
-        p.k2_bytes = span_bytes(second->k.S, second->k.sS, second->k.D);
-        p.Sk2 = second->k.S;
-        p.ds_nkg2 = ds_key_groups(second->k.S);
-        p.ds2 = (uint16_t*)second->ds;
-        p.km2 = second->km ? second->km->data : nullptr;
-    }
+    auto add = [&](const ra_tensor& kc, const void* dsc, const KeyMask* kmc) {
+        const int j = p.n_dqs++;
+        p.dqs_k[j] = (const uint16_t*)kc.data;
+        p.dqs_kbytes[j] = span_bytes(kc.S, kc.sS, kc.D);
+        p.dqs_Sk[j] = kc.S;
+        p.dqs_nkg[j] = ds_key_groups(kc.S);
+        p.dqs_ds[j] = (const uint16_t*)dsc;
+        p.dqs_km[j] = kmc ? kmc->data : nullptr;
+    };
+    add(k, ds, km);
+    for (int i = 0; i < n_more && p.n_dqs < kDqsMaxChunks; ++i)
+        if (more[i].k.S > 0) add(more[i].k, more[i].ds, more[i].km);
     p.dq = (float*)dq_acc.data;
     p.dq_sB = dq_acc.sB; p.dq_sS = dq_acc.sS; p.dq_sH = dq_acc.sH;
     p.dq_read = dq_read ? 1 : 0;

@@ -626,28 +626,38 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
         const ra_tensor dko = seq_slice(*dk, chunks->start[c], chunks->len[c]);
         const ra_tensor dvo = seq_slice(*dv, chunks->start[c], chunks->len[c]);
         if (single && i + 1 < steps.size()) {
-            // Two chunks per dQ pass when both dS fit the region (the second after the
-            // first): the dQ accumulator is then read and written once per pair of chunks.
-            const int c2 = steps[i + 1].c;
-            const int64_t off2 = (int64_t)round256((size_t)ra::ds_bytes(q->B, q->H, q->S, chunks->len[c]));
-            if (off2 + ra::ds_bytes(q->B, q->H, q->S, chunks->len[c2]) <= ds_room) {
-                void* const ds2 = (char*)ds + off2;
-                const ra_tensor kc2 = seq_slice(*k, chunks->start[c2], chunks->len[c2]);
-                const ra_tensor vc2 = seq_slice(*v, chunks->start[c2], chunks->len[c2]);
-                const ra_tensor dkc2 = seq_slice(dk_acc, chunks->start[c2], chunks->len[c2]);
-                const ra_tensor dvc2 = seq_slice(dv_acc, chunks->start[c2], chunks->len[c2]);
-                const ra_tensor dko2 = seq_slice(*dk, chunks->start[c2], chunks->len[c2]);
-                const ra_tensor dvo2 = seq_slice(*dv, chunks->start[c2], chunks->len[c2]);
-                const ra::KeyMask km2 = key_mask(kmask, chunks->start[c2]);
-                RA_HIP(ra::launch_bwd_dkdv_bf16(*q, kc, vc, *dout, *lse, delta, km, scale, dkc, dvc, ds, s,
-                                                direct_kv ? &dko : nullptr, direct_kv ? &dvo : nullptr));
-                RA_HIP(ra::launch_bwd_dkdv_bf16(*q, kc2, vc2, *dout, *lse, delta, km2, scale, dkc2, dvc2, ds2, s,
-                                                direct_kv ? &dko2 : nullptr, direct_kv ? &dvo2 : nullptr));
-                const ra::DqsChunk second{kc2, ds2, km2.data ? &km2 : nullptr};
+            // Several chunks per dQ pass: the dS of each chunk of the group is stored after
+            // the previous one's (as many as the region holds, at most kDqsMaxChunks), and
+            // one pass sweeps them all, so the dQ accumulator is read and written once per
+            // group instead of once per chunk.
+            size_t n = 1;
+            int64_t used = (int64_t)round256((size_t)ra::ds_bytes(q->B, q->H, q->S, chunks->len[c]));
+            while (i + n < steps.size() && n < (size_t)ra::kDqsMaxChunks) {
+                const int64_t b = ra::ds_bytes(q->B, q->H, q->S, chunks->len[steps[i + n].c]);
+                if (used + b > ds_room) break;
+                used += (int64_t)round256((size_t)b);
+                ++n;
+            }
+            if (n > 1) {
+                ra::KeyMask kms[ra::kDqsMaxChunks];
+                ra::DqsChunk more[ra::kDqsMaxChunks - 1];
+                char* dsj = (char*)ds;
+                for (size_t j = 0; j < n; ++j) {
+                    const int cj = steps[i + j].c;
+                    const int32_t st = chunks->start[cj], len = chunks->len[cj];
+                    const ra_tensor kcj = seq_slice(*k, st, len), vcj = seq_slice(*v, st, len);
+                    const ra_tensor dkj = seq_slice(dk_acc, st, len), dvj = seq_slice(dv_acc, st, len);
+                    const ra_tensor dkoj = seq_slice(*dk, st, len), dvoj = seq_slice(*dv, st, len);
+                    kms[j] = key_mask(kmask, st);
+                    RA_HIP(ra::launch_bwd_dkdv_bf16(*q, kcj, vcj, *dout, *lse, delta, kms[j], scale, dkj, dvj, dsj, s,
+                                                    direct_kv ? &dkoj : nullptr, direct_kv ? &dvoj : nullptr));
+                    if (j > 0) more[j - 1] = ra::DqsChunk{kcj, dsj, kms[j].data ? &kms[j] : nullptr};
+                    dsj += round256((size_t)ra::ds_bytes(q->B, q->H, q->S, len));
+                }
                 RA_HIP(ra::launch_bwd_dqs_bf16(*q, kc, ds, scale, dq_acc, s, !(direct_dq && i == 0),
-                                               direct_dq && i + 2 == steps.size() ? dq : nullptr,
-                                               km.data ? &km : nullptr, &second));
-                ++i;
+                                               direct_dq && i + n == steps.size() ? dq : nullptr,
+                                               kms[0].data ? &kms[0] : nullptr, more, (int)n - 1));
+                i += n - 1;
                 continue;
             }
         }

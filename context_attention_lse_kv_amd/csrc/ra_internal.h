@@ -30,6 +30,7 @@ inline int64_t ds_bytes(int B, int Hq, int Sq, int Sk) {
 }
 // the dQ pass over stored dS: kDqsWaves wavefronts, one 64-row query tile each, per workgroup
 constexpr int kDqsWaves = 8;
+constexpr int kDqsMaxChunks = 8;  // chunks one dQ pass can sweep
 inline int64_t dqs_workgroups(int B, int Hq, int Sq) {
     return (int64_t)B * Hq * ((ds_query_tiles(Sq) + kDqsWaves - 1) / kDqsWaves);
 }
@@ -73,9 +74,10 @@ hipError_t launch_bwd_dkdv_bf16(const ra_tensor& q, const ra_tensor& k, const ra
 // q rows and chunk k.  dq_read = false: dq_acc counts as zero (it is only written);
 // dq_out (bf16): when given, the sum is final and written there instead of dq_acc.
 // km: the chunk's key mask the dS was stored under (its masked keys hold zero dS), or
-// null; with it the pass skips the key tiles after the last valid key.  second: another
-// chunk (rows of the same k tensor, same q rows) whose dS is swept after the first one's
-// in the same pass, so that dq_acc is read and written once for both.
+// null; with it the pass skips the key tiles after the last valid key.  more: up to
+// kDqsMaxChunks - 1 further chunks (rows of the same k tensor, same q rows) whose dS is
+// swept after the first one's in the same pass, so that dq_acc is read and written once
+// for all of them.
 struct DqsChunk {
     ra_tensor k;
     const void* ds;
@@ -84,7 +86,7 @@ struct DqsChunk {
 hipError_t launch_bwd_dqs_bf16(const ra_tensor& q, const ra_tensor& k, const void* ds, float scale,
                                const ra_tensor& dq_acc, hipStream_t s, bool dq_read = true,
                                const ra_tensor* dq_out = nullptr, const KeyMask* km = nullptr,
-                               const DqsChunk* second = nullptr);
+                               const DqsChunk* more = nullptr, int n_more = 0);
 hipError_t launch_bwd_dq_bf16(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v, const ra_tensor& dout,
                               const ra_lse& lse, const ra_lse& delta, const KeyMask& km, float scale,
                               const ra_tensor& dq_acc, hipStream_t s);

@@ -74,7 +74,7 @@ def test_stored_ds_route_matches_oracle_and_ring(case):
     dq_r, dk_r, dv_r = ra.ring_bwd(gq, gk, gv, out, gdo, lse, ch, grad_dtype=torch.float32, kmask=gm)
     dq, dk, dv = _chunk_steps(gq, gk, gv, gdo, out, lse, gm, lens, order, "ds")
     # the ring runs these very kernels in this order (one query slice): dK/dV bit for bit;
-    # its dQ pass takes two chunks at a time, so dQ adds each pair's products in the
+    # its dQ pass sweeps the dS of several chunks at once, so dQ sums their products in the
     # kernel's fp32 accumulator before one add to dq (the chunk entry point adds per
     # chunk): equal up to fp32 rounding
     for a, b in ((dk, dk_r), (dv, dv_r)):

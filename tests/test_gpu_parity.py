@@ -210,17 +210,19 @@ def test_exchange_bit_exact_properties():
         grads = ra.head_to_seq([2 * y for y in ys], [S_loc] * g["ranks"])
         for x, gr in zip(shards, grads):
             assert torch.equal(gr, 2 * x)
-    # uneven seq and head splits, batch-first layout, bitwise against the oracle
-    for (seq_lens, heads) in (([334, 333, 333], [3, 3, 2]), ([5, 0, 4, 3], [1, 2, 2, 3])):
-        H = sum(heads)
-        xs = [W.randn((2, s, H, 64), seed=30 + i, dtype="bf16").to(d) for i, s in enumerate(seq_lens)]
-        ys = ra.seq_to_head(xs, heads, layout="bshd")
-        ref = oracle.seq_to_head([np.transpose(x.cpu().view(torch.int16).numpy(), (1, 0, 2, 3)) for x in xs], heads)
-        for y, rr in zip(ys, ref):
-            assert np.array_equal(np.transpose(y.cpu().view(torch.int16).numpy(), (1, 0, 2, 3)), rr)
-        back = ra.head_to_seq(ys, seq_lens, layout="bshd")
-        for x, b in zip(xs, back):
-            assert torch.equal(x, b)
+    # uneven seq and head splits, batch-first layout, bitwise against the oracle (16-byte
+    # vectors per row: 8 for bf16 D64, 16 for bf16 D128, 32 for fp32 D128)
+    for D, dt, bits in ((64, "bf16", torch.int16), (128, "bf16", torch.int16), (128, "f32", torch.int32)):
+        for (seq_lens, heads) in (([334, 333, 333], [3, 3, 2]), ([5, 0, 4, 3], [1, 2, 2, 3])):
+            H = sum(heads)
+            xs = [W.randn((2, s, H, D), seed=30 + i, dtype=dt).to(d) for i, s in enumerate(seq_lens)]
+            ys = ra.seq_to_head(xs, heads, layout="bshd")
+            ref = oracle.seq_to_head([np.transpose(x.cpu().view(bits).numpy(), (1, 0, 2, 3)) for x in xs], heads)
+            for y, rr in zip(ys, ref):
+                assert np.array_equal(np.transpose(y.cpu().view(bits).numpy(), (1, 0, 2, 3)), rr)
+            back = ra.head_to_seq(ys, seq_lens, layout="bshd")
+            for x, b in zip(xs, back):
+                assert torch.equal(x, b)
 
 
 # ------------------------------------------------------------------ image-DiT forward (D128, 4 chunks)

@@ -621,10 +621,12 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     constexpr int SMEMB = 6 * TILEB;                                  // [Q0 | dO0 | Q1 | dO1 | Q2 | dO2]
     constexpr int STATB = 3 * 2 * BM * 4;                             // [buffer][lse*log2e | delta][row]
     constexpr int PBUFB = 2 * kBwdWaves * 2 * RB * 64 * 16;           // [buffer][group][rb, t2][lane] (8 fp16 each)
-    __shared__ __attribute__((aligned(1024))) char smem[SMEMB + STATB + PBUFB];
+    constexpr int ZB = 16;                                            // zero slot (never written after the clear)
+    __shared__ __attribute__((aligned(1024))) char smem[SMEMB + STATB + PBUFB + ZB];
     RA_LDS char* const lbase = (RA_LDS char*)smem;
     RA_LDS float* const stat = (RA_LDS float*)(lbase + SMEMB);
     RA_LDS u32x4_t* const pbuf = (RA_LDS u32x4_t*)(lbase + SMEMB + STATB);
+    const RA_LDS float* const zslot = (const RA_LDS float*)(lbase + SMEMB + STATB + PBUFB);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -647,7 +649,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     const int ntiles = ntq * p.G;          // every Q tile of every query head of the group
 
     // zero all of LDS (the "tile -1" step and stale reads see finite values)
-    for (int i = tid; i < (SMEMB + STATB + PBUFB) / 16; i += 64 * NW) ((RA_LDS u32x4_t*)lbase)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = tid; i < (SMEMB + STATB + PBUFB + ZB) / 16; i += 64 * NW) ((RA_LDS u32x4_t*)lbase)[i] = u32x4_t{0u, 0u, 0u, 0u};
 
     // role 0 holds its keys' K rows, role 1 their V rows (the B operand of S or dP)
     bf16x8_t kvreg[KS];
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     auto commit_stats = [&](int buf) {
         if (tid < BM) {
             stat[(2 * buf) * BM + tid] = lpre * kLog2e;
-            stat[(2 * buf + 1) * BM + tid] = dpre;
+            stat[(2 * buf + 1) * BM + tid] = -dpre;  // role 1 starts its dP accumulator at -delta
         }
     };
 
@@ -753,27 +755,42 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         const RA_LDS u32x4_t* const pr = pbuf + (((it + 1) & 1) * kBwdWaves + kg) * (2 * RB) * 64 + lane;  // P of tile t-1
 
         if (role == 1) {
-            // dS of tile t-1 from its dP (still in sacc), P (fp16 from LDS) and delta
+            // dS of tile t-1 = P (dP - delta): sacc holds dP - delta (the accumulator
+            // started at -delta), P comes from LDS in fp16; one mixed-precision FMA per
+            // score (v_fma_mix_f32 reads either fp16 half of the packed word)
+            u32x4_t ph[RB][2];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int t2 = 0; t2 < 2; ++t2) {
-                    const u32x4_t ph = pr[(2 * rb + t2) * 64];
+                for (int t2 = 0; t2 < 2; ++t2) ph[rb][t2] = pr[(2 * rb + t2) * 64];
+            __builtin_amdgcn_sched_barrier(0);  // all four reads in flight before the first use
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int g4 = 2 * t2 + u;
-                        const f32x4_t dl = *(const RA_LDS f32x4_t*)&stat[(2 * prv + 1) * BM + 32 * rb + 8 * g4 + 4 * hh];
                         float dsv[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const uint32_t word = ph[2 * u + j / 2];
+                            const uint32_t word = ph[rb][t2][2 * u + j / 2];
                             const float pv = (float)__builtin_bit_cast(_Float16, (uint16_t)(j % 2 ? word >> 16 : word & 0xffffu));
-                            dsv[j] = pv * (sacc[rb][4 * g4 + j] - dl[j]);
+                            dsv[j] = __builtin_fmaf(pv, sacc[rb][4 * g4 + j], 0.f);
                         }
                         pk[rb][t2][2 * u] = pack_bf16x2(dsv[0], dsv[1]);
                         pk[rb][t2][2 * u + 1] = pack_bf16x2(dsv[2], dsv[3]);
                     }
-                }
+            // a key past the chunk or masked out: its dS is zeroed (the stored dS must be
+            // zero for the dQ pass; its own dK row is never written, so dK is unaffected)
+            if (ds_zap) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pk[rb][t2][i] &= ds_keep;
+            }
             if (p.ds != nullptr && it > 0) {
                 // dS of tile t-1 for the dQ pass: block (head, 32-key group, tile), sub-block
                 // grp = 16-row group, then key row (32 B: the lane pair's two 16-byte packs).
@@ -781,23 +798,11 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                 char* blk = (char*)p.ds +
                             ((((int64_t)b * p.Hq + ds_h) * p.ds_nkg + n0 / 32 + kg) * p.ds_nqt + ds_t) * 4096 +
                             l32 * 32 + hh * 16;
-                if (ds_zap) {
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                        for (int t2 = 0; t2 < 2; ++t2) {
-                            const u32x4_t v = pk[rb][t2];
-                            __builtin_nontemporal_store(
-                                u32x4_t{v[0] & ds_keep, v[1] & ds_keep, v[2] & ds_keep, v[3] & ds_keep},
-                                (u32x4_t*)(blk + (2 * rb + t2) * 1024));
-                        }
-                } else {
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int t2 = 0; t2 < 2; ++t2)
-                            __builtin_nontemporal_store(pk[rb][t2], (u32x4_t*)(blk + (2 * rb + t2) * 1024));
-                }
+                    for (int t2 = 0; t2 < 2; ++t2)
+                        __builtin_nontemporal_store(pk[rb][t2], (u32x4_t*)(blk + (2 * rb + t2) * 1024));
                 if (++ds_t == ntq) {
                     ds_t = 0;
                     ++ds_h;
@@ -805,6 +810,18 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+
+        // Accumulator starts of tile t (register 4 g4 + j = row 32 rb + 8 g4 + 4 hh + j):
+        // role 1's dP accumulates onto -delta of its rows, role 0's S onto zero (a
+        // broadcast read of a zero slot, so that both roles run the same code)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4_t c0 = *(const RA_LDS f32x4_t*)(role == 0 ? zslot : &stat[(2 * cur + 1) * BM + 32 * rb + 8 * g4 + 4 * hh]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sacc[rb][4 * g4 + j] = c0[j];
+            }
 
         {
             bf16x8_t st[NSLOT];
@@ -829,7 +846,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                 const int rb = s / KS, ks = s % KS, grp = s / DB, db = s % DB;
                 acc[db] = mfma32(as_bf16x8(pk[grp / 2][grp % 2]),
                                  as_bf16x8(u32x4_t{tr[s][0][0], tr[s][0][1], tr[s][1][0], tr[s][1][1]}), acc[db]);
-                sacc[rb] = mfma32(st[s], kvreg[ks], ks == 0 ? f32x16_t{} : sacc[rb]);
+                sacc[rb] = mfma32(st[s], kvreg[ks], sacc[rb]);
                 if (s + PF < NSLOT) row_read(s + PF);
                 if (s + LT < NSLOT) tr_read(s + LT);
                 __builtin_amdgcn_sched_barrier(0);
@@ -840,6 +857,12 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         if (role == 0) {
             // P of tile t: bf16 packs for the next iteration's dV, fp16 copy for role 1
             // lane = key, register 4 g4 + j = query row 32 rb + 8 g4 + 4 hh + j
+            f32x4_t l2v[RB][4];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) l2v[rb][g4] = *(const RA_LDS f32x4_t*)&stat[(2 * cur) * BM + 32 * rb + 8 * g4 + 4 * hh];
+            __builtin_amdgcn_sched_barrier(0);  // all eight reads in flight before the first use
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -848,7 +871,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int g4 = 2 * t2 + u;
-                        const f32x4_t l2 = *(const RA_LDS f32x4_t*)&stat[(2 * cur) * BM + 32 * rb + 8 * g4 + 4 * hh];
+                        const f32x4_t l2 = l2v[rb][g4];
                         float pv[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));

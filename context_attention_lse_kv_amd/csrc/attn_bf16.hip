@@ -670,18 +670,21 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     }
     float lpre = 0.f, dpre = 0.f;
     // Tiles are copied in order: tile it is Q tile it % ntq of query head g G + it / ntq,
-    // tracked incrementally (no division per tile) by (iss_h, iss_t).
-    int iss_h = g * p.G, iss_t = 0;
+    // tracked incrementally (no division or 64-bit product per tile): each copy's source
+    // is its head's slice base plus a 32-bit offset (a slice spans < 4 GiB) that grows by
+    // one tile per copy and restarts at the next head's slice.  A copied tile always
+    // starts inside its slice, so the offset never exceeds the slice's size.
+    const char* q_head = (const char*)(p.q + (int64_t)b * p.q_sB + (int64_t)(g * p.G) * p.q_sH);
+    const char* o_head = (const char*)(p.dout + (int64_t)b * p.do_sB + (int64_t)(g * p.G) * p.do_sH);
+    const char* l_head = (const char*)(p.lse + (int64_t)b * p.l_sB + (int64_t)(g * p.G) * p.l_sH);
+    const char* d_head = (const char*)(p.delta + (int64_t)b * p.d_sB + (int64_t)(g * p.G) * p.d_sH);
+    const uint32_t q_tstep = (uint32_t)(BM * p.q_sS * 2), o_tstep = (uint32_t)(BM * p.do_sS * 2);
+    const uint32_t lrow_bytes = (uint32_t)p.Sq * 4;
+    uint32_t q_off = 0, o_off = 0, l_off = 0;
+    int iss_t = 0;
     auto issue = [&](int buf) {
-        const int hq = iss_h, r0 = iss_t * BM;
-        if (++iss_t == ntq) {
-            iss_t = 0;
-            ++iss_h;
-        }
-        const uint16_t* qbase = p.q + (int64_t)b * p.q_sB + (int64_t)hq * p.q_sH;
-        const uint16_t* obase = p.dout + (int64_t)b * p.do_sB + (int64_t)hq * p.do_sH;
-        const i32x4_t rq = tile_desc(qbase, r0, p.q_sS * 2, p.q_bytes);
-        const i32x4_t ro = tile_desc(obase, r0, p.do_sS * 2, p.do_bytes);
+        const i32x4_t rq = make_desc(q_head + q_off, p.q_bytes - q_off);
+        const i32x4_t ro = make_desc(o_head + o_off, p.do_bytes - o_off);
         RA_LDS char* qdst = lbase + (2 * buf) * TILEB;
         RA_LDS char* odst = lbase + (2 * buf + 1) * TILEB;
 #pragma unroll
@@ -690,11 +693,20 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
             dma16(ro, odst + (w * NI + i) * 1024, vo[i]);
         }
         if (tid < BM) {
-            const uint32_t nbytes = (uint32_t)p.Sq * 4;
-            const float* lrow = p.lse + (int64_t)b * p.l_sB + (int64_t)hq * p.l_sH;
-            const float* drow = p.delta + (int64_t)b * p.d_sB + (int64_t)hq * p.d_sH;
-            lpre = bload4f(tile_rsrc(lrow, r0, 4, nbytes), (uint32_t)tid * 4, 0);
-            dpre = bload4f(tile_rsrc(drow, r0, 4, nbytes), (uint32_t)tid * 4, 0);
+            lpre = bload4f(make_rsrc(l_head + l_off, lrow_bytes - l_off), (uint32_t)tid * 4, 0);
+            dpre = bload4f(make_rsrc(d_head + l_off, lrow_bytes - l_off), (uint32_t)tid * 4, 0);
+        }
+        if (++iss_t == ntq) {
+            iss_t = 0;
+            q_head += p.q_sH * 2;
+            o_head += p.do_sH * 2;
+            l_head += p.l_sH * 4;
+            d_head += p.d_sH * 4;
+            q_off = o_off = l_off = 0;
+        } else {
+            q_off += q_tstep;
+            o_off += o_tstep;
+            l_off += BM * 4;
         }
     };
     auto commit_stats = [&](int buf) {
@@ -743,7 +755,14 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     commit_stats(0);
     if (ntiles > 1) issue(1);
     __syncthreads();
-    int ds_h = g * p.G, ds_t = 0;  // query head and 64-row tile of tile t-1 (dS store)
+    // dS store of tile t-1: block (head, 32-key group, tile) of this group; within a head
+    // the tiles' blocks are consecutive, the next head's start ds_nkg * ds_nqt blocks on
+    char* ds_head = p.ds == nullptr ? nullptr
+                                    : (char*)p.ds + ((((int64_t)b * p.Hq + g * p.G) * p.ds_nkg + n0 / 32 + kg) * p.ds_nqt) * 4096;
+    const int64_t ds_hstep = (int64_t)p.ds_nkg * p.ds_nqt * 4096;
+    const uint32_t ds_lane = l32 * 32 + hh * 16;
+    uint32_t ds_off = 0;
+    int ds_t = 0;
     // iteration it uses buffer cur = it % 3 for tile t = it (tile t-1 sits in (cur + 2) % 3);
     // the body is instantiated per cur so that the LDS addresses fold into immediates
     auto iteration = [&](const int it, auto curc) {
@@ -795,9 +814,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                 // dS of tile t-1 for the dQ pass: block (head, 32-key group, tile), sub-block
                 // grp = 16-row group, then key row (32 B: the lane pair's two 16-byte packs).
                 // Non-temporal: the stream must not push the Q/dO tiles out of L2.
-                char* blk = (char*)p.ds +
-                            ((((int64_t)b * p.Hq + ds_h) * p.ds_nkg + n0 / 32 + kg) * p.ds_nqt + ds_t) * 4096 +
-                            l32 * 32 + hh * 16;
+                char* blk = ds_head + ds_off + ds_lane;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -805,7 +822,10 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
                         __builtin_nontemporal_store(pk[rb][t2], (u32x4_t*)(blk + (2 * rb + t2) * 1024));
                 if (++ds_t == ntq) {
                     ds_t = 0;
-                    ++ds_h;
+                    ds_head += ds_hstep;
+                    ds_off = 0;
+                } else {
+                    ds_off += 4096;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);

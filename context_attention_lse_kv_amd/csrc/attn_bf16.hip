@@ -598,7 +598,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
 // without atomics).  Each 32-key group has two wavefronts (two per SIMD) with split
 // roles, pipelined one Q tile apart so that each one's softmax arithmetic overlaps the
 // other's MFMAs.  Iteration t (closed by the one barrier of the iteration) runs
-//   role 0: dV += P^T dO of tile t-1, S = Q K^T of tile t, then P = exp2(S c - lse2)
+//   role 0: dV += P^T dO of tile t-1, S = Q K^T of tile t, then P = exp2(c (S - lse / scale))
 //           (bf16 packs for its own dV, fp16 copy to LDS for role 1);
 //   role 1: dS = P (dP - delta) of tile t-1 (P from LDS), dP = dO V^T of tile t, and
 //           dK += dS^T Q of tile t-1.
@@ -621,12 +621,10 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     constexpr int SMEMB = 6 * TILEB;                                  // [Q0 | dO0 | Q1 | dO1 | Q2 | dO2]
     constexpr int STATB = 3 * 2 * BM * 4;                             // [buffer][lse*log2e | delta][row]
     constexpr int PBUFB = 2 * kBwdWaves * 2 * RB * 64 * 16;           // [buffer][group][rb, t2][lane] (8 fp16 each)
-    constexpr int ZB = 16;                                            // zero slot (never written after the clear)
-    __shared__ __attribute__((aligned(1024))) char smem[SMEMB + STATB + PBUFB + ZB];
+    __shared__ __attribute__((aligned(1024))) char smem[SMEMB + STATB + PBUFB];
     RA_LDS char* const lbase = (RA_LDS char*)smem;
     RA_LDS float* const stat = (RA_LDS float*)(lbase + SMEMB);
     RA_LDS u32x4_t* const pbuf = (RA_LDS u32x4_t*)(lbase + SMEMB + STATB);
-    const RA_LDS float* const zslot = (const RA_LDS float*)(lbase + SMEMB + STATB + PBUFB);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -649,7 +647,7 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     const int ntiles = ntq * p.G;          // every Q tile of every query head of the group
 
     // zero all of LDS (the "tile -1" step and stale reads see finite values)
-    for (int i = tid; i < (SMEMB + STATB + PBUFB + ZB) / 16; i += 64 * NW) ((RA_LDS u32x4_t*)lbase)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = tid; i < (SMEMB + STATB + PBUFB) / 16; i += 64 * NW) ((RA_LDS u32x4_t*)lbase)[i] = u32x4_t{0u, 0u, 0u, 0u};
 
     // role 0 holds its keys' K rows, role 1 their V rows (the B operand of S or dP)
     bf16x8_t kvreg[KS];
@@ -711,8 +709,11 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
     };
     auto commit_stats = [&](int buf) {
         if (tid < BM) {
-            stat[(2 * buf) * BM + tid] = lpre * kLog2e;
-            stat[(2 * buf + 1) * BM + tid] = -dpre;  // role 1 starts its dP accumulator at -delta
+            // role 0 starts its S accumulator at -lse / scale, role 1 its dP accumulator at
+            // -delta (scale > 0 and >= 2^-100 is checked on the host, so -lse / scale is finite
+            // for every finite lse)
+            stat[(2 * buf) * BM + tid] = -lpre / p.scale;
+            stat[(2 * buf + 1) * BM + tid] = -dpre;
         }
     };
 
@@ -832,13 +833,13 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         }
 
         // Accumulator starts of tile t (register 4 g4 + j = row 32 rb + 8 g4 + 4 hh + j):
-        // role 1's dP accumulates onto -delta of its rows, role 0's S onto zero (a
-        // broadcast read of a zero slot, so that both roles run the same code)
+        // role 0's S accumulates onto -lse / scale of its rows (so that P = exp2(c S') with
+        // c = scale log2(e)), role 1's dP onto -delta
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4_t c0 = *(const RA_LDS f32x4_t*)(role == 0 ? zslot : &stat[(2 * cur + 1) * BM + 32 * rb + 8 * g4 + 4 * hh]);
+                const f32x4_t c0 = *(const RA_LDS f32x4_t*)&stat[(2 * cur + role) * BM + 32 * rb + 8 * g4 + 4 * hh];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sacc[rb][4 * g4 + j] = c0[j];
             }
@@ -877,12 +878,6 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         if (role == 0) {
             // P of tile t: bf16 packs for the next iteration's dV, fp16 copy for role 1
             // lane = key, register 4 g4 + j = query row 32 rb + 8 g4 + 4 hh + j
-            f32x4_t l2v[RB][4];
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) l2v[rb][g4] = *(const RA_LDS f32x4_t*)&stat[(2 * cur) * BM + 32 * rb + 8 * g4 + 4 * hh];
-            __builtin_amdgcn_sched_barrier(0);  // all eight reads in flight before the first use
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -891,10 +886,9 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
                         const int g4 = 2 * t2 + u;
-                        const f32x4_t l2 = l2v[rb][g4];
                         float pv[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rb][4 * g4 + j], p.c, -l2[j]));
+                        for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(sacc[rb][4 * g4 + j] * p.c);
                         pk[rb][t2][2 * u] = pack_bf16x2(pv[0], pv[1]);
                         pk[rb][t2][2 * u + 1] = pack_bf16x2(pv[2], pv[3]);
                         ph[2 * u] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));

@@ -129,7 +129,8 @@ ra_status check_span32(const ra_tensor& t, const char* name) {
 bool same_shape(const ra_tensor& a, const ra_tensor& b) { return a.B == b.B && a.S == b.S && a.H == b.H && a.D == b.D; }
 
 ra_status check_scale(float scale) {
-    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(RA_E_ARG, "scale must be finite and > 0 (got %g)", scale);
+    // lower bound: the dK/dV kernel forms -lse / scale, which must stay finite
+    if (!std::isfinite(scale) || !(scale >= 0x1p-100f)) return fail(RA_E_ARG, "scale must be finite and >= 2^-100 (got %g)", scale);
     return RA_OK;
 }
 

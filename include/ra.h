@@ -39,6 +39,8 @@
  * GQA: H_kv must divide H_q; query head h uses key/value head h / (H_q/H_kv).
  * Scale: the softmax scale is an argument; the Python binding passes
  *   1/sqrt(D) (the SDPA default of [P1] "Reproduction") when none is given.
+ *   It must be finite and >= 2^-100 (RA_E_ARG otherwise): the bf16 dK/dV
+ *   kernel starts its score accumulator at -lse / scale.
  *   There is no dropout, causal mode or general attention mask ([P4]
  *   "Testcase" calls attention with None, 0.0, False); none is offered, so
  *   none can be silently ignored.  The one mask offered is a key-validity

@@ -93,7 +93,7 @@ def test_gqa_divisibility_refused_with_page_message():
     ("mixed_dtype", abi.RA_E_DTYPE), ("d96", abi.RA_E_UNSUPPORTED), ("misaligned_ptr", abi.RA_E_ALIGN),
     ("misaligned_stride", abi.RA_E_ALIGN), ("batch_mismatch", abi.RA_E_SHAPE), ("headdim_mismatch", abi.RA_E_SHAPE),
     ("out_bf16", abi.RA_E_DTYPE), ("out_shape", abi.RA_E_SHAPE), ("lse_shape", abi.RA_E_SHAPE),
-    ("bad_merge", abi.RA_E_ARG), ("neg_scale", abi.RA_E_ARG), ("nan_scale", abi.RA_E_ARG),
+    ("bad_merge", abi.RA_E_ARG), ("neg_scale", abi.RA_E_ARG), ("nan_scale", abi.RA_E_ARG), ("tiny_scale", abi.RA_E_ARG),
     ("overlap", abi.RA_E_ARG), ("neg_stride", abi.RA_E_ARG), ("zero_heads", abi.RA_E_SHAPE),
 ])
 def test_fwd_chunk_refuses(case, status):
@@ -117,6 +117,7 @@ def test_fwd_chunk_refuses(case, status):
     if case == "bad_merge": merge = 2
     if case == "neg_scale": scale = -1.0
     if case == "nan_scale": scale = float("nan")
+    if case == "tiny_scale": scale = 2.0 ** -101
     if case == "overlap": q.sS = 8  # rows alias each other's heads
     if case == "neg_stride": q.sH = -64
     if case == "zero_heads": q.H = 0

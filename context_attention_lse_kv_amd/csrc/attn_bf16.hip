@@ -282,9 +282,13 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     // LDS: [K0 | V0 | K1 | V1]; K and V tile it live in buffer it & 1.  With the key mask,
     // kbyte[buf] is the mask byte of key (tile start + lane) of the K tile in that buffer.
     uint32_t kbyte[2] = {0u, 0u};
+    // Every copied tile starts inside the chunk (or the chunk is empty and tile 0 has
+    // offset 0), so its byte offset is below the slice's size and fits 32 bits.
+    const uint32_t k_tstep = (uint32_t)(BN * p.k_sS * 2), v_tstep = (uint32_t)(BN * p.v_sS * 2);
     auto issue_k = [&](int it, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const i32x4_t rk = tile_desc(kbase, it * BN, p.k_sS * 2, p.k_bytes);
+        const uint32_t off = (uint32_t)it * k_tstep;
+        const i32x4_t rk = make_desc((const char*)kbase + off, p.k_bytes - off);
         RA_LDS char* kdst = lbase + (2 * buf) * TILEB;
 #pragma unroll
         for (int i = 0; i < NI; ++i) dma16(rk, kdst + (w * NI + i) * 1024, vk[i]);
@@ -292,7 +296,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     };
     auto issue_v = [&](int it, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const i32x4_t rv = tile_desc(vbase, it * BN, p.v_sS * 2, p.v_bytes);
+        const uint32_t off = (uint32_t)it * v_tstep;
+        const i32x4_t rv = make_desc((const char*)vbase + off, p.v_bytes - off);
         RA_LDS char* vdst = lbase + (2 * buf + 1) * TILEB;
 #pragma unroll
         for (int i = 0; i < NI; ++i) dma16(rv, vdst + (w * NI + i) * 1024, vv[i]);
@@ -1202,24 +1207,36 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
     for (int i = 0; i < 4; ++i) vds[i] = (uint32_t)(((64 * i + lane) ^ (8 * (i & 1))) * 16);
 
     const uint32_t vk = copy_voff<D>(w, lane, p.k_sS);
-    int first[kDqsMaxChunks];  // first key tile of each chunk in the pass's tile order
-    // tile it (keys 32 t .. of its chunk) into stage it % kDqsStages: one K copy (first
-    // KCOPIES wavefronts) and the wavefront's own dS block
-    auto issue = [&](int it) {
-        RA_LDS char* st = lbase + (it % kDqsStages) * STB;
-        int j = 0, t = it;  // chunk of tile it and the tile's index within it
+    int ntk[kDqsMaxChunks];  // key tiles of each chunk
+    // Tiles are issued in order (it = 0, 1, ...): tile it is key tile t of chunk j, tracked
+    // incrementally.  Tile it goes to stage it % kDqsStages: one K copy (first KCOPIES
+    // wavefronts) and the wavefront's own dS block.  A copied K tile starts inside its
+    // chunk, so its byte offset is below the slice's size and fits 32 bits; the dS offset
+    // can pass the slab (tiles at or past ds_nqt), where the copy reads zeros.
+    int iss_j = 0, iss_t = 0;
+    Chunk iss_c = chunk_of(0);
+    const uint32_t k_tstep = (uint32_t)(BN * p.k_sS * 2);
+    const int64_t ds_tstep = (int64_t)p.ds_nqt * 4096;
+    auto ntk_of = [&](int j) {  // ntk[j] through selects (no dynamically indexed register array)
+        int n = 0;
 #pragma unroll
-        for (int jj = 1; jj < kDqsMaxChunks; ++jj)
-            if (jj < p.n_dqs && it >= first[jj]) {
-                j = jj;
-                t = it - first[jj];
-            }
-        const Chunk c = chunk_of(j);
-        if (copies_k) dma16(tile_desc(c.kbase, (int64_t)t * BN, p.k_sS * 2, c.kbytes), st + w * 1024, vk);
-        const int64_t off = ((int64_t)t * p.ds_nqt + qt) * 4096;
-        const i32x4_t rd = make_desc(c.slab + off, off < c.slab_bytes ? (uint32_t)(c.slab_bytes - off) : 0u);
+        for (int jj = 0; jj < kDqsMaxChunks; ++jj)
+            if (jj == j) n = ntk[jj];
+        return n;
+    };
+    auto issue = [&](int it) {
+        while (iss_t == ntk_of(iss_j)) {  // next chunk with key tiles (only existing tiles are issued)
+            iss_t = 0;
+            iss_c = chunk_of(++iss_j);
+        }
+        RA_LDS char* st = lbase + (it % kDqsStages) * STB;
+        const uint32_t koff = (uint32_t)iss_t * k_tstep;
+        if (copies_k) dma16(make_desc((const char*)iss_c.kbase + koff, iss_c.kbytes - koff), st + w * 1024, vk);
+        const int64_t off = iss_t * ds_tstep + (int64_t)qt * 4096;
+        const i32x4_t rd = make_desc(iss_c.slab + off, off < iss_c.slab_bytes ? (uint32_t)(iss_c.slab_bytes - off) : 0u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_once(rd, st + KTB + w * 4096 + i * 1024, vds[i]);
+        ++iss_t;
     };
     // lane-constant LDS offsets: K^T reads (as V^T in the forward) and dS^T reads
     const int sw_tr = swz<RC>(4 * hh + e4), sw_tr8 = swz<RC>(4 * hh + e4 + 8);
@@ -1281,8 +1298,8 @@ __global__ __launch_bounds__(64 * kDqsWaves, 1) void bwd_dqs_bf16_kernel(BwdPara
     int ntiles = 0;
 #pragma unroll
     for (int j = 0; j < kDqsMaxChunks; ++j) {
-        first[j] = ntiles;
-        if (j < p.n_dqs) ntiles += key_tiles(p.dqs_km[j], p.dqs_Sk[j]);
+        ntk[j] = j < p.n_dqs ? key_tiles(p.dqs_km[j], p.dqs_Sk[j]) : 0;
+        ntiles += ntk[j];
     }
 #pragma unroll
     for (int i = 0; i < kDqsStages - 1; ++i)

@@ -175,16 +175,31 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteTable tab) {
     ((u32x4_t*)dst)[v] = ((const u32x4_t*)src)[v];
 }
 
-// The same exchange for outputs of fewer than 2^31 vectors (32-bit index arithmetic):
-// each thread moves four vectors, kThreads apart so that every access of a wavefront
-// covers 1 KiB of consecutive vectors (5.5 TB/s on the video shard's exchange against
-// 5.2 for one vector per thread with 64-bit indexing; the non-temporal hint made it
-// slower).
-__global__ __launch_bounds__(kThreads) void permute4_kernel(PermuteTable tab) {
-    const int r = blockIdx.y;
+// The same exchange for outputs of fewer than 2^31 vectors, split into the (output r,
+// input z) sub-copies (blockIdx.y, blockIdx.z): each is a box of B x L rows x Hs heads x V
+// vectors copied between fixed row and head offsets, so a block needs no search for its
+// source, and a vector's (b, row, head, vector) comes from three multiply-high divisions
+// instead of integer divisions.  Each thread moves four vectors, kThreads apart (every
+// access of a wavefront covers 1 KiB of consecutive vectors when a row holds >= 64).
+__device__ __forceinline__ uint32_t udiv(uint32_t n, UDiv d) {
+    const uint32_t t = __umulhi(d.m, n);
+    return (t + ((n - t) >> d.s1)) >> d.s2;
+}
+
+__global__ __launch_bounds__(kThreads) void permute_box_kernel(PermuteTable tab) {
+    const int r = blockIdx.y, z = blockIdx.z;
     const ra_tensor& o = tab.out[r];
+    const ra_tensor& x = tab.in[z];
+    // dir 0 (seq -> head): rows of input shard z into output r at row off[z], heads
+    //   hoff[r] .. of the input; dir 1 (head -> seq): rows off[r] .. of input group z into
+    //   output r, at heads hoff[z] .. of the output
+    const bool d0 = tab.dir == 0;
+    const uint32_t Hs = (uint32_t)(d0 ? o.H : x.H), L = (uint32_t)(d0 ? x.S : o.S);
     const uint32_t V = (uint32_t)(o.D * tab.elem_bytes / 16);
-    const uint32_t nvec = (uint32_t)o.B * (uint32_t)o.S * (uint32_t)o.H * V;
+    const UDiv dh = tab.dh[d0 ? r : z], dl = tab.dl[d0 ? z : r];
+    const int64_t s_src0 = d0 ? 0 : tab.off[r], s_dst0 = d0 ? tab.off[z] : 0;
+    const int64_t h_src0 = d0 ? tab.hoff[r] : 0, h_dst0 = d0 ? 0 : tab.hoff[z];
+    const uint32_t nvec = (uint32_t)o.B * L * Hs * V;
     const u32x4_t* ps[4];
     u32x4_t* pd[4];
     bool ok[4];
@@ -192,34 +207,19 @@ __global__ __launch_bounds__(kThreads) void permute4_kernel(PermuteTable tab) {
     for (int j = 0; j < 4; ++j) {
         const uint32_t e = (4 * blockIdx.x + j) * kThreads + threadIdx.x;
         ok[j] = e < nvec;
-        const uint32_t v = e % V;
-        uint32_t rr = e / V;
-        const int h = (int)(rr % (uint32_t)o.H);
-        rr /= (uint32_t)o.H;
-        const int s = (int)(rr % (uint32_t)o.S);
-        const int b = (int)(rr / (uint32_t)o.S);
-        const char* src;
-        if (tab.dir == 0) {
-            int i_src = 0;
-            while (i_src + 1 < tab.n_in && s >= tab.off[i_src + 1]) ++i_src;
-            const ra_tensor& x = tab.in[i_src];
-            src = (const char*)x.data + toff(x, b, s - tab.off[i_src], tab.hoff[r] + h) * tab.elem_bytes;
-        } else {
-            int g = 0;
-            while (g + 1 < tab.n_in && h >= tab.hoff[g + 1]) ++g;
-            const ra_tensor& x = tab.in[g];
-            src = (const char*)x.data + toff(x, b, tab.off[r] + s, h - tab.hoff[g]) * tab.elem_bytes;
-        }
-        ps[j] = (const u32x4_t*)src + v;
-        pd[j] = (u32x4_t*)((char*)o.data + toff(o, b, s, h) * tab.elem_bytes) + v;
+        const uint32_t q1 = udiv(e, tab.dv), v = e - q1 * V;
+        const uint32_t q2 = udiv(q1, dh), h = q1 - q2 * Hs;
+        const uint32_t b = udiv(q2, dl), l = q2 - b * L;
+        ps[j] = (const u32x4_t*)((const char*)x.data + toff(x, b, s_src0 + l, h_src0 + h) * tab.elem_bytes) + v;
+        pd[j] = (u32x4_t*)((char*)o.data + toff(o, b, s_dst0 + l, h_dst0 + h) * tab.elem_bytes) + v;
     }
-    u32x4_t x[4];
+    u32x4_t xv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (ok[j]) x[j] = *ps[j];
+        if (ok[j]) xv[j] = *ps[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        if (ok[j]) *pd[j] = x[j];
+        if (ok[j]) *pd[j] = xv[j];
 }
 
 inline unsigned nblocks(int64_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
@@ -271,19 +271,40 @@ hipError_t launch_fill_rows(const ra_lse& t, float value, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_permute(const PermuteTable& tab, hipStream_t s) {
-    int64_t maxvec = 0;
+static UDiv make_udiv(uint32_t d) {
+    if (d == 0) return UDiv{0u, 0, 0};  // empty sub-copy: never used
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return UDiv{(uint32_t)m, (uint16_t)(l < 1 ? l : 1), (uint16_t)(l > 1 ? l - 1 : 0)};
+}
+
+hipError_t launch_permute(const PermuteTable& tab_in, hipStream_t s) {
+    int64_t maxvec = 0, maxbox = 0;
     bool by4 = true;
+    PermuteTable tab = tab_in;
+    const bool d0 = tab.dir == 0;
     for (int r = 0; r < tab.n_out; ++r) {
         const ra_tensor& o = tab.out[r];
         const int V = o.D * tab.elem_bytes / 16;
         const int64_t n = (int64_t)o.B * o.S * o.H * V;
         if (n > maxvec) maxvec = n;
         if (n >= (int64_t(1) << 31)) by4 = false;
+        for (int z = 0; z < tab.n_in; ++z) {
+            const ra_tensor& x = tab.in[z];
+            const int64_t box = (int64_t)o.B * (d0 ? x.S : o.S) * (d0 ? o.H : x.H) * V;
+            if (box > maxbox) maxbox = box;
+        }
     }
     if (maxvec == 0) return hipSuccess;
     if (by4) {
-        permute4_kernel<<<dim3((unsigned)((maxvec + 4 * kThreads - 1) / (4 * kThreads)), tab.n_out), kThreads, 0, s>>>(tab);
+        tab.dv = make_udiv((uint32_t)(tab.out[0].D * tab.elem_bytes / 16));
+        for (int i = 0; i < kMaxRanks; ++i) {
+            tab.dh[i] = make_udiv(i < tab.n_out ? (uint32_t)(d0 ? tab.out[i].H : tab.in[i].H) : 0u);
+            tab.dl[i] = make_udiv(i < tab.n_out ? (uint32_t)(d0 ? tab.in[i].S : tab.out[i].S) : 0u);
+        }
+        permute_box_kernel<<<dim3((unsigned)((maxbox + 4 * kThreads - 1) / (4 * kThreads)), tab.n_out, tab.n_in),
+                             kThreads, 0, s>>>(tab);
     } else {
         permute_kernel<<<dim3(nblocks(maxvec), tab.n_out), kThreads, 0, s>>>(tab);
     }

@@ -43,12 +43,23 @@ struct KeyMask {
     int64_t sB;
 };
 
+// Unsigned 32-bit division by an invariant d >= 1 as a multiply-high and two shifts
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", the
+// round-up method): q = (t + ((n - t) >> s1)) >> s2 with t = mulhi(m, n).
+struct UDiv {
+    uint32_t m;
+    uint16_t s1, s2;
+};
+
 struct PermuteTable {
     int32_t n_in, n_out, dir, elem_bytes;
     ra_tensor in[kMaxRanks];
     ra_tensor out[kMaxRanks];
     int32_t off[kMaxRanks + 1];  // seq offsets (dir 0: of inputs; dir 1: of outputs)
     int32_t hoff[kMaxRanks + 1]; // head offsets (dir 0: of outputs; dir 1: of inputs)
+    // filled by launch_permute: division by the 16-byte vectors per row, and per rank by the
+    // head count (dh) and row count (dl) of the (output, input) sub-copies
+    UDiv dv, dh[kMaxRanks], dl[kMaxRanks];
 };
 
 // All launchers enqueue on `s` and return hipGetLastError() of the launch.

@@ -13,18 +13,45 @@ __device__ __forceinline__ int64_t toff(const ra_tensor& t, int64_t b, int64_t s
     return b * t.sB + s * t.sS + h * t.sH;
 }
 
+// n / d for 32-bit n by a multiply-high with the host-computed reciprocal of d
+__device__ __forceinline__ uint32_t udiv(uint32_t n, UDiv d) {
+    const uint32_t t = __umulhi(d.m, n);
+    return (t + ((n - t) >> d.s1)) >> d.s2;
+}
+
+// Index i of a [B, S, H, n] iteration (n fastest) -> (b, s, h, j): by the reciprocals in
+// rd when the host found every index below 2^31 (rd.fast), else by 64-bit division.
+struct RowDivs {
+    UDiv dn, dh, ds;
+    int32_t fast;
+};
+__device__ __forceinline__ void split_index(int64_t i, int n, int H, int S, const RowDivs& rd, int& b, int& s, int& h,
+                                            int& j) {
+    if (rd.fast) {
+        const uint32_t e = (uint32_t)i;
+        const uint32_t q1 = udiv(e, rd.dn), q2 = udiv(q1, rd.dh), q3 = udiv(q2, rd.ds);
+        j = (int)(e - q1 * (uint32_t)n);
+        h = (int)(q1 - q2 * (uint32_t)H);
+        s = (int)(q2 - q3 * (uint32_t)S);
+        b = (int)q3;
+    } else {
+        j = (int)(i % n);
+        int64_t r = i / n;
+        h = (int)(r % H);
+        r /= H;
+        s = (int)(r % S);
+        b = (int)(r / S);
+    }
+}
+
 // ---------------------------------------------------------------- LSE merge
 // One thread per (row, 4 consecutive d).  lse = log(e^a + e^b); both -inf -> (0, -inf).
 __global__ __launch_bounds__(kThreads) void merge_lse_kernel(ra_tensor oa, ra_lse la, ra_tensor ob, ra_lse lb,
-                                                             int64_t nvec) {
+                                                             int64_t nvec, RowDivs rd) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= nvec) return;
-    const int D4 = oa.D / 4;
-    const int d4 = (int)(i % D4);
-    int64_t r = i / D4;
-    const int h = (int)(r % oa.H); r /= oa.H;
-    const int s = (int)(r % oa.S);
-    const int b = (int)(r / oa.S);
+    int b, s, h, d4;
+    split_index(i, oa.D / 4, oa.H, oa.S, rd, b, s, h, d4);
     float* pa_l = la.data + (int64_t)b * la.sB + (int64_t)h * la.sH + s;
     const float a = *pa_l;
     const float bb = lb.data[(int64_t)b * lb.sB + (int64_t)h * lb.sH + s];
@@ -82,18 +109,15 @@ __device__ __forceinline__ float dot8<float, uint16_t>(const void* po, const voi
 
 // D/8 lanes per row, 8 elements each, reduced with lane shuffles.
 template <typename TO, typename TD>
-__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(ra_tensor o, ra_tensor dout, ra_lse delta, int64_t nrows) {
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(ra_tensor o, ra_tensor dout, ra_lse delta, int64_t nrows,
+                                                             RowDivs rd) {
     const int L = o.D / 8;  // lanes per row: 8 or 16
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t row = gid / L;
-    const int part = (int)(gid % L);
+    const int64_t row = gid >> __builtin_ctz(L);  // L = D / 8 is 8 or 16
     float s = 0.f;
-    int b = 0, h = 0, sq = 0;
+    int b = 0, h = 0, sq = 0, part = 0;
     if (row < nrows) {
-        int64_t r = row;
-        h = (int)(r % o.H); r /= o.H;
-        sq = (int)(r % o.S);
-        b = (int)(r / o.S);
+        split_index(gid, L, o.H, o.S, rd, b, sq, h, part);
         const TO* po = (const TO*)o.data + toff(o, b, sq, h) + part * 8;
         const TD* pd = (const TD*)dout.data + toff(dout, b, sq, h) + part * 8;
         s = dot8<TO, TD>(po, pd);
@@ -181,11 +205,6 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(PermuteTable tab) {
 // source, and a vector's (b, row, head, vector) comes from three multiply-high divisions
 // instead of integer divisions.  Each thread moves four vectors, kThreads apart (every
 // access of a wavefront covers 1 KiB of consecutive vectors when a row holds >= 64).
-__device__ __forceinline__ uint32_t udiv(uint32_t n, UDiv d) {
-    const uint32_t t = __umulhi(d.m, n);
-    return (t + ((n - t) >> d.s1)) >> d.s2;
-}
-
 __global__ __launch_bounds__(kThreads) void permute_box_kernel(PermuteTable tab) {
     const int r = blockIdx.y, z = blockIdx.z;
     const ra_tensor& o = tab.out[r];
@@ -226,11 +245,31 @@ inline unsigned nblocks(int64_t n) { return (unsigned)((n + kThreads - 1) / kThr
 
 }  // namespace
 
+static UDiv make_udiv(uint32_t d) {
+    if (d == 0) return UDiv{0u, 0, 0};  // empty extent: never used
+    int l = 0;
+    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return UDiv{(uint32_t)m, (uint16_t)(l < 1 ? l : 1), (uint16_t)(l > 1 ? l - 1 : 0)};
+}
+
+// reciprocals for split_index over nidx indices of a [B, S, H, n] iteration
+static RowDivs row_divs(int64_t nidx, int n, int H, int S) {
+    RowDivs rd{};
+    rd.fast = nidx < (int64_t(1) << 31) ? 1 : 0;
+    if (rd.fast) {
+        rd.dn = make_udiv((uint32_t)n);
+        rd.dh = make_udiv((uint32_t)H);
+        rd.ds = make_udiv((uint32_t)S);
+    }
+    return rd;
+}
+
 hipError_t launch_merge_lse(const ra_tensor& oa, const ra_lse& la, const ra_tensor& ob, const ra_lse& lb,
                             hipStream_t s) {
     const int64_t nvec = (int64_t)oa.B * oa.S * oa.H * (oa.D / 4);
     if (nvec == 0) return hipSuccess;
-    merge_lse_kernel<<<nblocks(nvec), kThreads, 0, s>>>(oa, la, ob, lb, nvec);
+    merge_lse_kernel<<<nblocks(nvec), kThreads, 0, s>>>(oa, la, ob, lb, nvec, row_divs(nvec, oa.D / 4, oa.H, oa.S));
     return hipGetLastError();
 }
 
@@ -239,12 +278,13 @@ hipError_t launch_bwd_delta(const ra_tensor& o, const ra_tensor& dout, const ra_
     if (nrows == 0) return hipSuccess;
     const int64_t nthr = nrows * (o.D / 8);
     const unsigned g = nblocks(nthr);
+    const RowDivs rd = row_divs((int64_t)g * kThreads, o.D / 8, o.H, o.S);
     if (o.dtype == RA_F32 && dout.dtype == RA_F32)
-        bwd_delta_kernel<float, float><<<g, kThreads, 0, s>>>(o, dout, delta, nrows);
+        bwd_delta_kernel<float, float><<<g, kThreads, 0, s>>>(o, dout, delta, nrows, rd);
     else if (o.dtype == RA_BF16 && dout.dtype == RA_BF16)
-        bwd_delta_kernel<uint16_t, uint16_t><<<g, kThreads, 0, s>>>(o, dout, delta, nrows);
+        bwd_delta_kernel<uint16_t, uint16_t><<<g, kThreads, 0, s>>>(o, dout, delta, nrows, rd);
     else if (o.dtype == RA_F32 && dout.dtype == RA_BF16)
-        bwd_delta_kernel<float, uint16_t><<<g, kThreads, 0, s>>>(o, dout, delta, nrows);
+        bwd_delta_kernel<float, uint16_t><<<g, kThreads, 0, s>>>(o, dout, delta, nrows, rd);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -269,14 +309,6 @@ hipError_t launch_fill_rows(const ra_lse& t, float value, hipStream_t s) {
     if (n == 0) return hipSuccess;
     fill_rows_kernel<<<nblocks(n), kThreads, 0, s>>>(t, value, n);
     return hipGetLastError();
-}
-
-static UDiv make_udiv(uint32_t d) {
-    if (d == 0) return UDiv{0u, 0, 0};  // empty sub-copy: never used
-    int l = 0;
-    while ((uint64_t(1) << l) < d) ++l;  // ceil(log2 d)
-    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
-    return UDiv{(uint32_t)m, (uint16_t)(l < 1 ? l : 1), (uint16_t)(l > 1 ? l - 1 : 0)};
 }
 
 hipError_t launch_permute(const PermuteTable& tab_in, hipStream_t s) {

@@ -298,7 +298,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the ring; --gpus {args.gpus} is not supported "
-              "(single-GPU build: no collectives)", file=sys.stderr)
+              "(the library runs on one GPU and has no collectives)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X (HIP device)", file=sys.stderr)

@@ -283,6 +283,8 @@ ra_status check_bwd_chunk(const ra_tensor* q, const ra_tensor* k, const ra_tenso
     RA_TRY(check_tensor(dout, "dout"));
     if (dout->dtype != q->dtype) return fail(RA_E_DTYPE, "dout must have the dtype of q");
     if (!same_shape(*dout, *q)) return fail(RA_E_SHAPE, "dout must have the shape of q");
+    // dout may have strides of its own: its slices get the same 32-bit bound as q's
+    if (q->dtype == RA_BF16) RA_TRY(check_span32(*dout, "dout"));
     RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
     RA_TRY(check_rows(delta, "delta", q->B, q->H, q->S));
     RA_TRY(check_scale(scale));
@@ -556,6 +558,7 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     if (!same_shape(*out, *q) || !same_shape(*dout, *q)) return fail(RA_E_SHAPE, "out and dout must have the shape of q");
     if (dout->dtype != q->dtype) return fail(RA_E_DTYPE, "dout must have the dtype of q");
     if (out->dtype == RA_BF16 && dout->dtype == RA_F32) return fail(RA_E_DTYPE, "bf16 out with fp32 dout is not supported");
+    if (q->dtype == RA_BF16) RA_TRY(check_span32(*dout, "dout"));
     RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
     RA_TRY(check_scale(scale));
     RA_TRY(check_chunks(chunks, k->S));

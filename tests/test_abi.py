@@ -300,3 +300,25 @@ def test_masked_entry_points_validate_the_rest_as_before():
     q, k, v, o, l = good(Hq=6, Hkv=4)
     assert lib.ra_fwd_chunk_masked(q, k, v, None, 0.125, o, l, 0, None) == abi.RA_E_SHAPE
     assert golden()["gqa_divisibility_error"]["message"] in lib.ra_last_error().decode()
+
+
+def test_bwd_refuses_dout_slice_past_32bit_span():
+    """The bf16 backward kernels address a (batch, head) slice of dout with 32-bit buffer
+    offsets, as for q: a dout whose own strides make one slice span 2^31 bytes or more is
+    refused before any launch, even when q's slices are small."""
+    lib = _lib()
+    B, S, Hq, Hkv, D = 1, 40000, 4, 4, 128
+    q, k, v = T(B, S, Hq, D), T(B, S, Hkv, D), T(B, S, Hkv, D)
+    wide = T(B, S, Hq, D, strides=(S * 65536, 65536, D))  # 5.2 GB per slice
+    l = Lrows(B, Hq, S)
+    acc_q, acc_k = T(B, S, Hq, D, abi.RA_F32), T(B, S, Hkv, D, abi.RA_F32)
+    st = lib.ra_bwd_chunk(q, k, v, wide, l, l, 0.125, acc_q, acc_k, acc_k, 1, None)
+    assert st == abi.RA_E_UNSUPPORTED and "dout" in lib.ra_last_error().decode()
+    assert lib.ra_bwd_chunk(q, k, v, q, l, l, 0.125, acc_q, acc_k, acc_k, 2, None) == abi.RA_E_ARG  # same call, dout ok
+    need = lib.ra_bwd_ds_bytes(q, k)
+    st = lib.ra_bwd_chunk_dkdv_ds(q, k, v, wide, l, l, None, 0.125, acc_k, acc_k, 1, FAKE, need, None)
+    assert st == abi.RA_E_UNSUPPORTED
+    c = chunks([20000, 20000], [0, 1])
+    o = T(B, S, Hq, D)
+    st = lib.ra_ring_bwd(q, k, v, o, wide, l, ctypes.byref(c), 0.125, o, k, v, None, 0, None)
+    assert st == abi.RA_E_UNSUPPORTED and "dout" in lib.ra_last_error().decode()

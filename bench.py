@@ -105,8 +105,9 @@ def run_workload(full, steps, warmup, masked=False, single=False):
     t_fwd = timed(fwd, max(3, steps // 2), 1)
     t_bwd = timed(bwd, max(3, steps // 2), 1)
     f_f, f_b = flops(w.B, w.Hq, q.shape[1], w.S, w.D)
-    return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, t_step=t_step, t_fwd=t_fwd,
-                t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step, step_ms=step_ms)
+    return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
+                t_step=t_step, t_fwd=t_fwd, t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step, bwd=bwd,
+                step_ms=step_ms)
 
 
 def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
@@ -150,6 +151,53 @@ def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
     torch.cuda.synchronize()
     t = sum(a.elapsed_time(b) for a, b in ev) / launches / 1e3
     return t, f
+
+
+def forward_kernel(r, lead_steps=3):
+    """The forward chunk step as the ring sweep runs it after its first step: one launch of
+    fwd_bf16_kernel<128, MERGE> per chunk, each merging its partial into the running fp32
+    (output, LSE) state in its epilogue.  The shard's 7 merging launches (chunks in ring
+    order after the local one) run back to back, each between a HIP event pair on the
+    stream, after `lead_steps` whole ring steps queued without a host synchronisation
+    (the clock settles only under sustained load).  4*D flop per (query row, key, head)."""
+    q, k, v = r["q"], r["k"], r["v"]
+    lens, order = r["lens"], r["order"]
+    starts = [sum(lens[:i]) for i in range(len(lens))]
+    acc = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty_like(r["lse"])
+    c0 = order[0]
+    ra.fwd_chunk(q, k[:, starts[c0]:starts[c0] + lens[c0]], v[:, starts[c0]:starts[c0] + lens[c0]], acc, lse, merge=0)
+    s = torch.cuda.current_stream()
+    rest = order[1:]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in rest]
+    torch.cuda.synchronize()
+    for _ in range(lead_steps):
+        r["step"]()
+    for (a, b), c in zip(ev, rest):
+        a.record(s)
+        ra.fwd_chunk(q, k[:, starts[c]:starts[c] + lens[c]], v[:, starts[c]:starts[c] + lens[c]], acc, lse, merge=1)
+        b.record(s)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+    w = r["w"]
+    return t, 4.0 * w.B * w.Hq * q.shape[1] * lens[rest[0]] * w.D
+
+
+def backward_sweep_events(r, reps=6, lead_steps=2):
+    """Median HIP-event duration (s) of one ring backward sweep of the shard, each sweep
+    between an event pair, after `lead_steps` whole ring steps."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for _ in range(lead_steps):
+        r["step"]()
+    for a, b in ev:
+        a.record(s)
+        r["bwd"]()
+        b.record(s)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return ts[len(ts) // 2] / 1e3
 
 
 def image_dit_fwd(steps=20, warmup=3):
@@ -218,18 +266,19 @@ def hbm_kernels(r, reps=10):
 
 
 KERNEL_SRC = os.path.join(ROOT, "context_attention_lse_kv_amd", "csrc", "attn_bf16.hip")
-PROFILE = os.path.join(ROOT, "profiles", "bwd_kv_bf16_video_dit_shard.md")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter profile,
-    or None when the kernel source has changed since the counters were taken."""
+def measured_traffic(profile):
+    """HBM bytes per launch of a kernel from its committed counter profile (the
+    machine-readable lines at its end), or None when the kernel source has changed since
+    the counters were taken (or the profile holds no counter figure)."""
     import hashlib
     try:
         with open(KERNEL_SRC, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()[:16]
         vals = {}
-        with open(PROFILE) as f:
+        with open(os.path.join(PROFILES, profile)) as f:
             for line in f:
                 if ":" in line:
                     k, _, v = line.partition(":")
@@ -241,11 +290,44 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(target_s=10.0):
+def roofline_entry(kernel, flop, seconds, method_bytes, profile, note=None):
+    """One matrix-core kernel against the bf16 MFMA peak.  `method_bytes`: the HBM bytes
+    the method itself needs for the launch (its inputs read once, its outputs written
+    once); `traffic`: what the hardware counters measured for it (FETCH_SIZE + WRITE_SIZE,
+    calibrated), and `traffic_ratio` = traffic / method_bytes (well above 1: bytes the
+    route moves that the method does not need)."""
+    achieved = flop / seconds / 1e12
+    traffic = measured_traffic(profile)
+    e = {"bound": "mfma", "kernel": kernel, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(seconds * 1e3, 4),
+         "method_flop": flop, "method_bytes": int(method_bytes), "traffic": traffic,
+         "traffic_ratio": None if traffic is None else round(traffic / method_bytes, 2)}
+    if note:
+        e["note"] = note
+    return e
+
+
+def snapshot(r, groups=2):
+    """Host copies of the timed step's results for the first `groups` kv-head groups (their
+    query heads' out, lse, dq; their kv heads' dk, dv), for the parity check of the CPU
+    baseline leg."""
+    w = r["w"]
+    nh = groups * (w.Hq // w.Hkv)
+    f = lambda t: t.float().cpu()
+    return {"groups": groups, "out": f(r["out"][:, :, :nh]), "lse": r["lse"][:, :nh].cpu(),
+            "dq": f(r["dq"][:, :, :nh]), "dk": f(r["dk"][:, :, :groups]), "dv": f(r["dv"][:, :, :groups])}
+
+
+def cpu_baseline(snap, target_s=10.0):
     """The CPU fp64 oracle, as it stands, on a bounded sample of the workload: whole
-    query heads of the rank-0 shard (4096 rows each, against all 32768 keys of the
-    head's kv head), forward + backward, one head after another until at least
-    `target_s` seconds have been spent."""
+    kv-head groups of the rank-0 shard (each group = its 4 query heads, 4096 rows each,
+    against all 32768 keys of the group's kv head), forward + backward, one group after
+    another until at least `target_s` seconds have been spent (at most the groups in
+    `snap`).  Its results are compared with the timed step's (`snap`): the parity record
+    carries the whole-tensor relative error of the diffusers issue "Ring attention
+    backward uses stale iteration-0 KV" (section Reproduction), the worst single D-vector
+    and the max-abs error of out/dq/dk/dv, and the LSE's max abs error, against the gates
+    (bf16 2e-2, LSE 1e-3)."""
     import numpy as np
     import oracle
     try:
@@ -257,17 +339,46 @@ def cpu_baseline(target_s=10.0):
     q, k, v, do = W.make_inputs(w, Sq=4096)
     f64 = lambda t: t.float().numpy().astype(np.float64)
     G = w.Hq // w.Hkv
-    heads, spent = 0, 0.0
-    while spent < target_s and heads < w.Hq:
-        h = heads
-        qn, don = f64(q[:, :, h:h + 1]), f64(do[:, :, h:h + 1])
-        kn, vn = f64(k[:, :, h // G:h // G + 1]), f64(v[:, :, h // G:h // G + 1])
-        t0 = time.perf_counter()
-        oracle.attention_forward(qn, kn, vn, row_block=256)
-        oracle.attention_backward(qn, kn, vn, don, row_block=256)
-        spent += time.perf_counter() - t0
-        heads += 1
+    ref = {"out": [], "lse": [], "dq": [], "dk": [], "dv": []}
+    groups, spent = 0, 0.0
+    while groups < snap["groups"] and (groups == 0 or spent < target_s):
+        g = groups
+        kn, vn = f64(k[:, :, g:g + 1]), f64(v[:, :, g:g + 1])
+        dk_g, dv_g = 0.0, 0.0
+        for h in range(g * G, (g + 1) * G):
+            qn, don = f64(q[:, :, h:h + 1]), f64(do[:, :, h:h + 1])
+            t0 = time.perf_counter()
+            o, l = oracle.attention_forward(qn, kn, vn, row_block=256)
+            dq_, dk_, dv_ = oracle.attention_backward(qn, kn, vn, don, row_block=256)
+            spent += time.perf_counter() - t0
+            ref["out"].append(o[:, :, 0]); ref["lse"].append(l[:, 0]); ref["dq"].append(dq_[:, :, 0])
+            dk_g = dk_g + dk_[:, :, 0]
+            dv_g = dv_g + dv_[:, :, 0]
+        ref["dk"].append(dk_g); ref["dv"].append(dv_g)
+        groups += 1
+    heads = groups * G
     fl = 14.0 * heads * q.shape[1] * w.S * w.D
+
+    def rel(a, b):
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    def worst_vec(a, b):
+        e = np.linalg.norm((a - b).reshape(-1, a.shape[-1]), axis=1)
+        n = np.linalg.norm(b.reshape(-1, b.shape[-1]), axis=1)
+        return float((e / np.maximum(n, 0.25 * np.sqrt(np.mean(n * n)))).max())
+
+    par = {"sample": f"kv-head groups 0..{groups - 1} (query heads 0..{heads - 1}) of the timed step", "tensors": {}}
+    for name, axis in (("out", 2), ("dq", 2), ("dk", 2), ("dv", 2)):
+        want = np.stack(ref[name], axis=axis)
+        got = snap[name].numpy().astype(np.float64)[:, :, :want.shape[2]]
+        par["tensors"][name] = {"rel": round(rel(got, want), 6), "worst_vector": round(worst_vec(got, want), 6),
+                                "max_abs": round(float(np.abs(got - want).max()), 6)}
+    want_l = np.stack(ref["lse"], axis=1)
+    got_l = snap["lse"].numpy().astype(np.float64)[:, :heads]
+    par["lse_max_abs"] = round(float(np.abs(got_l - want_l).max()), 8)
+    par["gates"] = {"rel": 2e-2, "worst_vector": 2e-2, "lse_max_abs": 1e-3}
+    par["pass"] = bool(all(t["rel"] <= 2e-2 and t["worst_vector"] <= 2e-2 for t in par["tensors"].values())
+                       and par["lse_max_abs"] <= 1e-3)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -276,9 +387,10 @@ def cpu_baseline(target_s=10.0):
         pass
     return {"value": round(fl / spent / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "host": {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas_threads": threads},
-            "sample": f"oracle fwd+bwd (numpy fp64) of query heads 0..{heads - 1} of the rank-0 shard "
-                      f"({q.shape[1]} rows each, all {w.S} keys of the head's kv head); {spent:.1f} s wall; "
-                      f"same 14*Sq*Sk*D flop count"}
+            "sample": f"oracle fwd+bwd (numpy fp64) of kv-head groups 0..{groups - 1} (query heads 0..{heads - 1}) "
+                      f"of the rank-0 shard ({q.shape[1]} rows each, all {w.S} keys of the group's kv head); "
+                      f"{spent:.1f} s wall; same 14*Sq*Sk*D flop count",
+            "parity": par}
 
 
 def main():
@@ -322,9 +434,35 @@ def main():
     r = run_workload(False, args.steps, args.warmup)
     total = r["f_f"] + r["f_b"]
     value = total / r["t_step"] / 1e12
+    w = r["w"]
+    B, Sq, Hq, Hkv, D, Sc = w.B, int(r["q"].shape[1]), w.Hq, w.Hkv, w.D, r["lens"][0]
+    n_ch = len(r["lens"])
+    # the method's HBM bytes per launch: inputs read once, outputs written once (bf16 = 2 B, fp32 = 4 B)
+    q_b, kv_b, st_b = B * Sq * Hq * D * 2, B * Sc * Hkv * D * 2, B * Hq * Sq * 4
     t_k, f_k = dominant_kernel(r)
     t_after_dq, _ = dominant_kernel(r, back_to_back=False)
-    achieved = f_k / t_k / 1e12
+    t_f, f_f1 = forward_kernel(r)
+    t_bwd_ev = backward_sweep_events(r)
+    snap = None if args.no_cpu_baseline else snapshot(r)
+    dkdv = roofline_entry(
+        "bwd_kv_bf16_kernel<128> (dK/dV of one ring step, storing dS: 4096 q rows x 4096 keys x 32 heads)",
+        f_k, t_k, 2 * q_b + 2 * kv_b + 2 * st_b + 2 * kv_b, "bwd_kv_bf16_video_dit_shard.md",
+        note="method bytes: Q, dO, K_j, V_j, lse, delta read; dK_j, dV_j (bf16) written.  The dS this route "
+             "stores for the dQ pass (2 B per query row, key and head) is route traffic, not method bytes")
+    dkdv["avg_launch_ms_after_dq_pass"] = round(t_after_dq * 1e3, 4)
+    fwd = roofline_entry(
+        "fwd_bf16_kernel<128, merge> (one ring step merging into the running state: 4096 q rows x 4096 keys x 32 heads)",
+        f_f1, t_f, q_b + 2 * kv_b + 2 * (2 * q_b + st_b), "fwd_bf16_video_dit_shard.md",
+        note="method bytes: Q, K_j, V_j read; the running fp32 output and LSE read and written (the LSE merge)")
+    # the dQ pass: one launch per backward sweep over the dS of all chunks; its time is the sweep's
+    # HIP-event time minus its 8 dK/dV launches (back to back, as above) and delta (hbm_kernels)
+    res_hbm = hbm_kernels(r)
+    t_dq = t_bwd_ev - n_ch * t_k - res_hbm["bwd_delta"]["ms"] / 1e3
+    dqp = roofline_entry(
+        "bwd_dqs_bf16_kernel<128> (dQ of the whole backward sweep from the stored dS of its 8 chunks)",
+        2.0 * B * Hq * Sq * w.S * D, t_dq, n_ch * kv_b + q_b, "bwd_dqs_bf16_video_dit_shard.md",
+        note="time derived: backward sweep (HIP events) minus its dK/dV launches and delta; method bytes: K of "
+             "every chunk read, dq (bf16) written.  The route also reads the stored dS (8 GiB per sweep)")
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -338,8 +476,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "video_dit_gqa_rank0_shard", "B": 1, "S": r["w"].S, "Sq": int(r["q"].shape[1]),
-                   "Hq": r["w"].Hq, "Hkv": r["w"].Hkv, "D": r["w"].D, "chunks": r["lens"], "order": r["order"],
+        "config": {"workload": "video_dit_gqa_rank0_shard", "B": 1, "S": w.S, "Sq": Sq,
+                   "Hq": Hq, "Hkv": Hkv, "D": D, "chunks": r["lens"], "order": r["order"],
                    "inputs": "N(0,1) seed 777, bf16"},
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(r["f_f"] / r["t_fwd"] / 1e12, 2),
@@ -348,13 +486,10 @@ def main():
                            "min": round(min(r["step_ms"]), 4), "max": round(max(r["step_ms"]), 4)},
         "fwd_ms": round(r["t_fwd"] * 1e3, 4),
         "bwd_ms": round(r["t_bwd"] * 1e3, 4),
-        "roofline": {"bound": "mfma", "kernel": "bwd_kv_bf16_kernel<128> (dK/dV of one ring step, storing dS: 4096 q rows x 4096 keys x 32 heads)",
-                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(t_k * 1e3, 4),
-                     "avg_launch_ms_after_dq_pass": round(t_after_dq * 1e3, 4),
-                     "traffic": measured_traffic()},
+        "roofline": dkdv,
+        "rooflines": [dkdv, fwd, dqp],
     }
-    res["hbm_kernels"] = hbm_kernels(r)
+    res["hbm_kernels"] = res_hbm
     del r
     torch.cuda.empty_cache()
     if not args.no_full:
@@ -391,7 +526,7 @@ def main():
     if not args.no_image:
         res["image_dit_fwd"] = image_dit_fwd()
         torch.cuda.empty_cache()
-    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline()
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(snap)
     print(json.dumps(res), flush=True)
 
 

@@ -52,8 +52,10 @@ int64_t numel(const ra_tensor& t) { return (int64_t)t.B * t.S * t.H * t.D; }
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// True if no two logical elements of the tensor share an address.
+// True if no two logical elements of the tensor share an address (trivially so for a
+// tensor with no elements, whatever its strides).
 bool non_overlapping(const ra_tensor& t) {
+    if (numel(t) == 0) return true;
     struct Dim { int64_t stride, extent; };
     std::vector<Dim> dims = {{1, t.D}, {t.sH, t.H}, {t.sS, t.S}, {t.sB, t.B}};
     dims.erase(std::remove_if(dims.begin(), dims.end(), [](const Dim& d) { return d.extent <= 1; }), dims.end());
@@ -472,9 +474,10 @@ size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
     return round256((size_t)numel(*q) * 4);
 }
 
-// dS region of the bf16 ring backward: enough for every query row against the whole key
-// sequence, capped at kDsBudget; a chunk whose dS does not fit is swept in query-row
-// slices (multiples of 64 rows) that do.
+// dS region of the bf16 ring backward that ra_ring_bwd_workspace_bytes recommends: enough
+// for every query row against the whole key sequence, capped at kDsBudget.  The sweep
+// itself uses whatever room the caller's workspace leaves above the minimum: a chunk whose
+// dS does not fit is swept in query-row slices (multiples of 64 rows) that do.
 static constexpr int64_t kDsBudget = int64_t(8) << 30;
 // a sliced chunk keeps the stored-dS route only while each slice's dQ pass has at least
 // this many workgroups (one per compute unit)
@@ -486,16 +489,112 @@ static size_t ds_region_bytes(const ra_tensor& q, const ra_tensor& k) {
     return round256((size_t)(full < kDsBudget ? full : kDsBudget));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Plan of the ring backward for a given workspace size.  Per chunk (in sweep order), the
+// stored-dS route with query slices of `rows` rows, or the recompute route (rows = 0).
+// fp32 accumulators are carved from the workspace only for bf16 gradients that need one:
+// dK/dV when some chunk is swept in more than one slice (else each chunk's rows are final
+// after its one dK/dV launch and are written in bf16 directly), dQ unless one dQ pass
+// covers the dS of every chunk (it then writes the bf16 dq directly).
+struct BwdStep {
+    int c;
+    int32_t rows;
+};
+struct BwdPlan {
+    std::vector<BwdStep> steps;
+    bool single = false;     // every chunk in one slice on the stored-dS route
+    bool one_group = false;  // ... and one dQ pass covers all of them
+    bool dq_acc = false, dk_acc = false, dv_acc = false;
+    size_t delta_b = 0, dq_b = 0, dk_b = 0, dv_b = 0;
+    size_t fixed() const {
+        return delta_b + (dq_acc ? dq_b : 0) + (dk_acc ? dk_b : 0) + (dv_acc ? dv_b : 0);
+    }
+};
+
+void plan_steps(BwdPlan& P, const ra_tensor& q, const ra_chunks& ch, int64_t ds_room) {
+    P.steps.clear();
+    for (int i = 0; i < ch.n; ++i) {
+        const int c = ch.order[i];
+        if (ch.len[c] == 0 || q.S == 0) continue;
+        const int64_t per_tile = q.dtype == RA_BF16 ? ra::ds_bytes(q.B, q.H, 64, ch.len[c]) : 0;
+        const int64_t slab_rows = per_tile == 0 ? 0 : 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, ch.len[c]));
+        int32_t rows = per_tile == 0 || per_tile > ds_room
+                           ? 0
+                           : (int32_t)std::min<int64_t>({64 * (ds_room / per_tile), slab_rows, (int64_t)q.S});
+        if (rows > 0 && rows < q.S && ra::dqs_workgroups(q.B, q.H, rows) < kMinSliceWorkgroups) rows = 0;
+        P.steps.push_back({c, rows});
+    }
+    P.single = !P.steps.empty();
+    for (const BwdStep& st : P.steps) P.single = P.single && st.rows >= q.S;
+    int64_t all = 0;
+    for (const BwdStep& st : P.steps) all += (int64_t)round256((size_t)ra::ds_bytes(q.B, q.H, q.S, ch.len[st.c]));
+    P.one_group = P.single && P.steps.size() <= (size_t)ra::kDqsMaxChunks && all <= ds_room;
+}
+
+// The plan for a workspace of ws_bytes (SIZE_MAX: the recommended size, with a dS region
+// of ds_region_bytes).  Accumulators are carved first and the dS room is what is left; as
+// less room can only need more accumulators, three rounds settle it.
+BwdPlan plan_bwd(const ra_tensor& q, const ra_tensor& k, const ra_chunks& ch, const ra_tensor& dq,
+                 const ra_tensor& dk, const ra_tensor& dv, size_t ws_bytes) {
+    BwdPlan P;
+    P.delta_b = round256((size_t)q.B * q.H * q.S * 4);
+    P.dq_b = round256((size_t)numel(q) * 4);
+    P.dk_b = P.dv_b = round256((size_t)numel(k) * 4);
+    const bool rec = ws_bytes == SIZE_MAX;
+    for (int round = 0; round < 4; ++round) {
+        const size_t f = P.fixed();
+        const int64_t room = rec ? (int64_t)ds_region_bytes(q, k)
+                                 : (ws_bytes > f ? (int64_t)((ws_bytes - f) & ~(size_t)255) : 0);
+        plan_steps(P, q, ch, room);
+        const bool ndq = dq.dtype == RA_BF16 && !P.one_group;
+        const bool nkv = !(P.single && dk.dtype == RA_BF16 && dv.dtype == RA_BF16);
+        const bool ndk = dk.dtype == RA_BF16 && nkv, ndv = dv.dtype == RA_BF16 && nkv;
+        if ((!ndq || P.dq_acc) && (!ndk || P.dk_acc) && (!ndv || P.dv_acc)) break;
+        P.dq_acc |= ndq;
+        P.dk_acc |= ndk;
+        P.dv_acc |= ndv;
+    }
+    return P;
+}
+
+// Plans for the workspace-size queries, which see no chunk table: the whole key
+// sequence as one chunk.
+ra_chunks one_chunk(const ra_tensor& k, int32_t* buf) {
+    buf[0] = 0;
+    buf[1] = k.S;
+    buf[2] = 0;
+    return ra_chunks{1, &buf[0], &buf[1], &buf[2]};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ra_ring_bwd_workspace_min_bytes(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq,
+                                       const ra_tensor* dk, const ra_tensor* dv) {
+    if (!q || !k) return 0;
+    const ra_tensor dq_ = dq ? *dq : *q, dk_ = dk ? *dk : *k, dv_ = dv ? *dv : *k;
+    int32_t buf[3];
+    const ra_chunks ch = one_chunk(*k, buf);
+    const BwdPlan P = plan_bwd(*q, *k, ch, dq_, dk_, dv_, 0);
+    return P.fixed();
+}
+
 size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq, const ra_tensor* dk,
                                    const ra_tensor* dv) {
     if (!q || !k) return 0;
-    size_t n = round256((size_t)q->B * q->H * q->S * 4);
-    if (dq && dq->dtype == RA_BF16) n += round256((size_t)numel(*q) * 4);
-    if (dk && dk->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
-    if (dv && dv->dtype == RA_BF16) n += round256((size_t)numel(*k) * 4);
-    n += ds_region_bytes(*q, *k);
-    return n;
+    const ra_tensor dq_ = dq ? *dq : *q, dk_ = dk ? *dk : *k, dv_ = dv ? *dv : *k;
+    int32_t buf[3];
+    const ra_chunks ch = one_chunk(*k, buf);
+    const BwdPlan P = plan_bwd(*q, *k, ch, dq_, dk_, dv_, SIZE_MAX);
+    // never below the size any chunk table is accepted with (a table whose plan needs
+    // every accumulator then still runs; accumulators its plan skips become dS room)
+    return std::max(P.fixed() + ds_region_bytes(*q, *k), ra_ring_bwd_workspace_min_bytes(q, k, dq, dk, dv));
 }
+
 
 static ra_lse rows_slice(const ra_lse& t, int32_t start, int32_t len) {
     ra_lse r = t;
@@ -567,44 +666,20 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     RA_TRY(check_tensor(dv, "dv"));
     if (!same_shape(*dq, *q) || !same_shape(*dk, *k) || !same_shape(*dv, *v))
         return fail(RA_E_SHAPE, "dq, dk, dv must have the shapes of q, k, v");
-    const size_t need = ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv);
-    RA_TRY(check_ws(ws, ws_bytes, need));
+    const BwdPlan P = plan_bwd(*q, *k, *chunks, *dq, *dk, *dv, ws_bytes);
+    RA_TRY(check_ws(ws, ws_bytes, P.fixed()));
     hipStream_t s = (hipStream_t)stream;
     char* p = (char*)ws;
     const ra_lse delta = contiguous_rows(p, q->B, q->H, q->S);
-    p += round256((size_t)q->B * q->H * q->S * 4);
+    p += P.delta_b;
     ra_tensor dq_acc = *dq, dk_acc = *dk, dv_acc = *dv;
-    if (dq->dtype == RA_BF16) { dq_acc = contiguous_f32(p, *q); p += round256((size_t)numel(*q) * 4); }
-    if (dk->dtype == RA_BF16) { dk_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
-    if (dv->dtype == RA_BF16) { dv_acc = contiguous_f32(p, *k); p += round256((size_t)numel(*k) * 4); }
+    if (P.dq_acc) { dq_acc = contiguous_f32(p, *q); p += P.dq_b; }
+    if (P.dk_acc) { dk_acc = contiguous_f32(p, *k); p += P.dk_b; }
+    if (P.dv_acc) { dv_acc = contiguous_f32(p, *k); p += P.dv_b; }
     void* const ds = p;
-    const int64_t ds_room = (int64_t)ds_region_bytes(*q, *k);
-
-    // Plan: per chunk, the stored-dS route with query slices of `rows` rows (the dS of a
-    // slice fits the region and one (batch, head) slab of it stays within the 2^31 bytes the
-    // dQ pass addresses with 32-bit buffer offsets), or the recompute route (rows = 0) when
-    // slices would be so thin that the dQ pass could not fill the chip.
-    struct Step {
-        int c;
-        int32_t rows;
-    };
-    std::vector<Step> steps;
-    for (int i = 0; i < chunks->n; ++i) {
-        const int c = chunks->order[i];
-        if (chunks->len[c] == 0 || q->S == 0) continue;
-        const int64_t per_tile = q->dtype == RA_BF16 ? ra::ds_bytes(q->B, q->H, 64, chunks->len[c]) : 0;
-        const int64_t slab_rows = per_tile == 0 ? 0 : 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, chunks->len[c]));
-        int32_t rows = per_tile == 0 || per_tile > ds_room
-                           ? 0
-                           : (int32_t)std::min<int64_t>({64 * (ds_room / per_tile), slab_rows, (int64_t)q->S});
-        if (rows > 0 && rows < q->S && ra::dqs_workgroups(q->B, q->H, rows) < kMinSliceWorkgroups) rows = 0;
-        steps.push_back({c, rows});
-    }
-    // When every chunk takes the stored-dS route in one slice, each chunk's dK/dV rows are
-    // final after its one dK/dV launch and dQ after the last dQ pass: bf16 outputs are then
-    // written directly (no zeroing of the fp32 accumulators, no casts at the end).
-    bool single = !steps.empty();
-    for (const Step& st : steps) single = single && st.rows >= q->S;
+    const int64_t ds_room = ws_bytes > P.fixed() ? (int64_t)((ws_bytes - P.fixed()) & ~(size_t)255) : 0;
+    const std::vector<BwdStep>& steps = P.steps;
+    const bool single = P.single;
     const bool direct_kv = single && dk->dtype == RA_BF16 && dv->dtype == RA_BF16;
     const bool direct_dq = single && dq->dtype == RA_BF16;
 

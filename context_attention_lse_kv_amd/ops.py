@@ -241,29 +241,34 @@ def ring_bwd(q, k, v, out, dout, lse, chunks, scale=None, grad_dtype=None, layou
     dk = torch.empty(k.shape, dtype=gd, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=gd, device=q.device) if dv is None else dv
     t = [tensor_desc(x, layout) for x in (q, k, v, out, dout, dq, dk, dv)]
-    need = lib().ra_ring_bwd_workspace_bytes(t[0], t[1], t[5], t[6], t[7])
-    ws = _workspace(workspace, need, q.device)
-    wsp = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    if workspace is None:
+        need = lib().ra_ring_bwd_workspace_bytes(t[0], t[1], t[5], t[6], t[7])
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    # the library plans from the room the workspace gives (at least the minimum size)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wsp = ctypes.c_void_p(workspace.data_ptr() if workspace is not None else 0)
     sc = _scale(scale, q.shape[-1])
     if kmask is None:
         check(lib().ra_ring_bwd(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), ctypes.byref(chunks.c), sc,
-                                t[5], t[6], t[7], wsp, need, _stream(q)), "ra_ring_bwd")
+                                t[5], t[6], t[7], wsp, nbytes, _stream(q)), "ra_ring_bwd")
     else:
         check(lib().ra_ring_bwd_masked(t[0], t[1], t[2], t[3], t[4], rows_desc(lse), kmask_desc(kmask),
-                                       ctypes.byref(chunks.c), sc, t[5], t[6], t[7], wsp, need, _stream(q)),
+                                       ctypes.byref(chunks.c), sc, t[5], t[6], t[7], wsp, nbytes, _stream(q)),
               "ra_ring_bwd_masked")
     return dq, dk, dv
 
 
-def ring_bwd_workspace_bytes(q, k, dq_dtype=None, dk_dtype=None, layout="bshd"):
-    """Workspace bytes ``ring_bwd`` needs for these q, k (gradients of dtype
-    ``dq_dtype`` / ``dk_dtype``, default q's dtype): delta, fp32 accumulators for bf16
-    gradients and, on the bf16 path, the dS region."""
+def ring_bwd_workspace_bytes(q, k, dq_dtype=None, dk_dtype=None, layout="bshd", minimum=False):
+    """Workspace bytes for ``ring_bwd`` with these q, k (gradients of dtype ``dq_dtype`` /
+    ``dk_dtype``, default q's dtype): the size at which it runs fastest (delta, the fp32
+    accumulators its plan needs and, on the bf16 path, the dS region), or with
+    ``minimum`` the least it accepts."""
     tq, tk = tensor_desc(q, layout), tensor_desc(k, layout)
     tdq, tdk = tensor_desc(q, layout), tensor_desc(k, layout)
     tdq.dtype = _DT[dq_dtype or q.dtype]
     tdk.dtype = _DT[dk_dtype or k.dtype]
-    return lib().ra_ring_bwd_workspace_bytes(tq, tk, tdq, tdk, tdk)
+    fn = lib().ra_ring_bwd_workspace_min_bytes if minimum else lib().ra_ring_bwd_workspace_bytes
+    return fn(tq, tk, tdq, tdk, tdk)
 
 
 def _workspace(ws, need, device):

@@ -230,15 +230,20 @@ ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
 
 /* Backward sweep: delta from (out, dout), then one chunk step per chunk in
  * the same order as the forward, each against its own chunk; dq, dk, dv
- * (bf16 or fp32, shapes of q, k, v) are written.  ws: at least
- * ra_ring_bwd_workspace_bytes(q, k, dq, dk, dv) bytes (delta, fp32
- * accumulators for any bf16 gradient and, for bf16 inputs, a dS region of at
- * most 8 GiB).  With bf16 inputs a chunk step computes the same quantities as
- * ra_bwd_chunk by another route: the dK/dV kernel stores dS = P (dP - delta)
- * in bf16 to the dS region and a second kernel forms dQ += scale dS K from it,
- * instead of recomputing S and dP (query rows go in slices when the dS of a
- * whole chunk does not fit the region).  Results agree with ra_bwd_chunk up to
- * rounding, not bit for bit. */
+ * (bf16 or fp32, shapes of q, k, v) are written.  ws: a device workspace of
+ * ws_bytes bytes (256-byte aligned), at least
+ * ra_ring_bwd_workspace_min_bytes(q, k, dq, dk, dv) (RA_E_WORKSPACE below
+ * that); ra_ring_bwd_workspace_bytes gives the size that runs fastest.  With
+ * bf16 inputs a chunk step computes the same quantities as ra_bwd_chunk by
+ * another route: the dK/dV kernel stores dS = P (dP - delta) in bf16 to the
+ * workspace and a second kernel forms dQ += scale dS K from it, instead of
+ * recomputing S and dP.  The sweep plans from the room ws_bytes leaves: query
+ * rows go in slices (multiples of 64) when the dS of a whole chunk does not fit,
+ * and a chunk whose slices would be too thin to fill the GPU takes the
+ * recompute route (ra_bwd_chunk's kernels); any plan gives the same result up
+ * to rounding.  fp32 accumulators for bf16 gradients are carved only where the
+ * plan needs them.  Results agree with ra_bwd_chunk up to rounding, not bit for
+ * bit. */
 ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
                       const ra_tensor* out, const ra_tensor* dout, const ra_lse* lse,
                       const ra_chunks* chunks, float scale,
@@ -256,9 +261,22 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
                              ra_tensor* dq, ra_tensor* dk, ra_tensor* dv,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace sizes.  ra_ring_fwd_workspace_bytes: what ra_ring_fwd needs.
+ * ra_ring_bwd_workspace_min_bytes: ra_ring_bwd accepts any workspace of at least
+ * this size with any chunk table: delta plus an fp32 accumulator for every bf16
+ * gradient (every chunk may then take the recompute route).  With a given chunk
+ * table a plan may need less (e.g. chunks small enough to keep the stored-dS
+ * route with no dK/dV accumulators); ra_ring_bwd refuses a workspace only when
+ * the plan it allows needs more than ws_bytes.  ra_ring_bwd_workspace_bytes: the
+ * size at which ra_ring_bwd runs fastest: delta, the fp32 accumulators its plan
+ * needs and a dS region of min(8 GiB, dS of every query row against the whole
+ * key sequence), and never less than the minimum.  dq/dk/dv give the gradient
+ * dtypes (NULL: the dtype of q/k/v). */
 size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out);
 size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k,
                                    const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);
+size_t ra_ring_bwd_workspace_min_bytes(const ra_tensor* q, const ra_tensor* k,
+                                       const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);
 
 /* ---------------------------------------------------------------- exchange */
 

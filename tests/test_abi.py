@@ -171,13 +171,41 @@ def test_ring_fwd_needs_workspace_for_bf16_out():
 
 
 def test_ring_bwd_workspace_sizes():
+    """Recommended size: delta + the dS region (+ only the accumulators that plan needs);
+    minimum: delta + an fp32 accumulator for every bf16 gradient, no dS region."""
     lib = _lib()
     q, k = T(1, 100, 8, 64), T(1, 300, 2, 64)
     f = lambda t: T(t.B, t.S, t.H, t.D, abi.RA_F32)
-    base = lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k))
-    assert base >= 8 * 100 * 4
-    full = lib.ra_ring_bwd_workspace_bytes(q, k, q, k, k)
-    assert full >= base + (100 * 8 * 64 + 2 * 300 * 2 * 64) * 4
+    r256 = lambda n: (n + 255) // 256 * 256
+    delta = r256(8 * 100 * 4)
+    ds = lib.ra_bwd_ds_bytes(q, k)
+    accs = r256(100 * 8 * 64 * 4) + 2 * r256(300 * 2 * 64 * 4)
+    # fp32 gradients are their own accumulators
+    assert lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k)) == delta + ds
+    assert lib.ra_ring_bwd_workspace_min_bytes(q, k, f(q), f(k), f(k)) == delta
+    # bf16 gradients: the whole dS fits the region, so one dQ pass writes dq and each dK/dV
+    # launch writes its rows in bf16 directly; the minimum carries every accumulator
+    assert lib.ra_ring_bwd_workspace_bytes(q, k, q, k, k) == delta + ds
+    assert lib.ra_ring_bwd_workspace_min_bytes(q, k, q, k, k) == delta + accs
+    # fp32 inputs: no dS route at all
+    q32, k32 = f(q), f(k)
+    assert lib.ra_ring_bwd_workspace_bytes(q32, k32, q32, k32, k32) == delta
+    assert lib.ra_ring_bwd_workspace_min_bytes(q32, k32, q, k, k) == delta + accs
+    # the video shard: 8 GiB of dS, no accumulators in the recommended plan
+    bq, bk = T(1, 4096, 32, 128), T(1, 32768, 8, 128)
+    assert lib.ra_ring_bwd_workspace_bytes(bq, bk, bq, bk, bk) == r256(32 * 4096 * 4) + (8 << 30)
+
+
+def test_ring_bwd_refuses_below_minimum_workspace():
+    lib = _lib()
+    q, k, v = T(1, 100, 8, 64), T(1, 300, 2, 64), T(1, 300, 2, 64)
+    l = Lrows(1, 8, 100)
+    c = chunks([150, 150], [1, 0])
+    need = lib.ra_ring_bwd_workspace_min_bytes(q, k, q, k, k)
+    st = lib.ra_ring_bwd(q, k, v, q, q, l, ctypes.byref(c), 0.125, q, k, v, FAKE, need - 256, None)
+    assert st == abi.RA_E_WORKSPACE and str(need) in lib.ra_last_error().decode()
+    assert lib.ra_ring_bwd(q, k, v, q, q, l, ctypes.byref(c), 0.125, q, k, v, None, 0, None) == abi.RA_E_WORKSPACE
+    assert lib.ra_ring_bwd(q, k, v, q, q, l, ctypes.byref(c), 0.125, q, k, v, FAKE + 16, need, None) == abi.RA_E_ALIGN
 
 
 def test_bwd_ds_bytes_and_ring_ds_region():
@@ -198,7 +226,7 @@ def test_bwd_ds_bytes_and_ring_ds_region():
     big_q, big_k = T(1, 32768, 32, 128), T(1, 32768, 8, 128)
     fq, fk = f(big_q), f(big_k)
     assert lib.ra_ring_bwd_workspace_bytes(big_q, big_k, fq, fk, fk) - \
-        lib.ra_ring_bwd_workspace_bytes(fq, fk, fq, fk, fk) == 8 << 30
+        lib.ra_ring_bwd_workspace_bytes(fq, fk, fq, fk, fk) == 8 << 30  # the 8 GiB cap of the region
 
 
 def test_stored_ds_entry_points_refuse():

@@ -12,7 +12,7 @@ import torch
 import context_attention_lse_kv_amd as ra
 import oracle
 import workloads as W
-from parity import BF16_TOL, LSE_TOL_BF16, dev, max_abs, np64, rel
+from parity import BF16_TOL, check_bf16, LSE_TOL_BF16, dev, max_abs, np64, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -50,9 +50,9 @@ def test_autograd_matches_ring_bwd_and_oracle():
     qn, kn, vn, don = (np64(t) for t in (q, k, v, do))
     o, _ = oracle.attention_forward(qn, kn, vn)
     g = oracle.attention_backward(qn, kn, vn, don)
-    assert rel(np64(out), o) <= BF16_TOL
+    check_bf16('out', np64(out), o)
     for a, b in zip(grads, g):
-        assert rel(np64(a), b) <= BF16_TOL
+        check_bf16('grad', np64(a), b)
 
 
 @pytest.mark.parametrize("masked", [False, True])
@@ -112,10 +112,10 @@ def test_compiled_ulysses_exchange_keeps_gradients():
     gq, gk, gv = oracle.attention_backward(to_b(q), to_b(k), to_b(v), to_b(do))
     cat = lambda ts: np.transpose(np64(torch.cat(ts, dim=0)), (1, 0, 2, 3))
     R = len(seq)
-    assert rel(cat(oc), o) <= BF16_TOL
-    assert rel(cat(gc[:R]), gq) <= BF16_TOL
-    assert rel(cat(gc[R:2 * R]), gk) <= BF16_TOL
-    assert rel(cat(gc[2 * R:]), gv) <= BF16_TOL
+    check_bf16('out', cat(oc), o)
+    check_bf16('dq', cat(gc[:R]), gq)
+    check_bf16('dk', cat(gc[R:2 * R]), gk)
+    check_bf16('dv', cat(gc[2 * R:]), gv)
 
 
 def test_allgather_single_chunk_sweep():
@@ -137,7 +137,9 @@ def test_allgather_single_chunk_sweep():
     qn, kn, vn, don = (np64(t) for t in (q[:, :, :4], k[:, :, :1], v[:, :, :1], do[:, :, :4]))
     o, l = oracle.attention_forward(qn, kn, vn)
     gq_, gk_, gv_ = oracle.attention_backward(qn, kn, vn, don)
-    assert rel(np64(o1[:, :, :4]), o) <= BF16_TOL and max_abs(np64(l1[:, :4]), l) <= LSE_TOL_BF16
-    assert rel(np64(g1[0][:, :, :4]), gq_) <= BF16_TOL
+    check_bf16('out', np64(o1[:, :, :4]), o)
+    assert max_abs(np64(l1[:, :4]), l) <= LSE_TOL_BF16
+    check_bf16('dq', np64(g1[0][:, :, :4]), gq_)
     # dK/dV of kv head 0 receive the sum over its 4 query heads, all included above
-    assert rel(np64(g1[1][:, :, :1]), gk_) <= BF16_TOL and rel(np64(g1[2][:, :, :1]), gv_) <= BF16_TOL
+    check_bf16('dk', np64(g1[1][:, :, :1]), gk_)
+    check_bf16('dv', np64(g1[2][:, :, :1]), gv_)

@@ -14,7 +14,7 @@ import torch
 import context_attention_lse_kv_amd as ra
 import oracle
 import workloads as W
-from parity import BF16_TOL, LSE_TOL_BF16, dev, max_abs, np64, oracle_by_head, rel
+from parity import BF16_TOL, check_bf16, LSE_TOL_BF16, dev, max_abs, np64, oracle_by_head, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +85,7 @@ def test_stored_ds_route_matches_oracle_and_ring(case):
     mn = None if m is None else m.numpy().astype(np.uint8)
     g = oracle.attention_backward(qn, kn, vn, don, kmask=mn)
     for a, b in zip((dq, dk, dv), g):
-        assert rel(np64(a), b) <= BF16_TOL, rel(np64(a), b)
+        check_bf16('grad', np64(a), b)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -152,9 +152,9 @@ def test_ring_bwd_sweeps_query_slices_when_ds_exceeds_region():
     qn, kn, vn, don = (np64(t) for t in (q[:, rows], k, v, do[:, rows]))
     ref = oracle_by_head(qn, kn, vn, don, heads)
     sel = lambda t: np64(t.cpu()[:, rows][:, :, heads])
-    assert rel(sel(out), ref["out"]) <= BF16_TOL
+    check_bf16('out', sel(out), ref["out"])
     assert max_abs(np64(lse.cpu()[:, heads][:, :, rows]), ref["lse"]) <= LSE_TOL_BF16
-    assert rel(sel(dq), ref["dq"]) <= BF16_TOL
+    check_bf16('dq', sel(dq), ref["dq"])
 
 
 @pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])

@@ -20,7 +20,7 @@ EXPORTS = [
     "ra_fwd_chunk", "ra_merge_lse", "ra_bwd_delta", "ra_bwd_chunk", "ra_bwd_chunk_dkdv", "ra_bwd_chunk_dq",
     "ra_ring_fwd", "ra_ring_bwd",
     "ra_fwd_chunk_masked", "ra_bwd_chunk_masked", "ra_bwd_chunk_dkdv_masked", "ra_bwd_chunk_dq_masked",
-    "ra_ring_fwd_masked", "ra_ring_bwd_masked",
+    "ra_ring_fwd_masked", "ra_ring_bwd_masked", "ra_ring_fwd_noalloc",
     "ra_bwd_ds_bytes", "ra_bwd_chunk_dkdv_ds", "ra_bwd_chunk_dq_ds",
     "ra_ring_fwd_workspace_bytes", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd_workspace_min_bytes",
     "ra_seq_head_permute",
@@ -70,6 +70,7 @@ _SIGS = {
     "ra_bwd_chunk_dq_masked": (i32, [T, T, T, T, L, L, K, f32, T, vp]),
     "ra_ring_fwd_masked": (i32, [T, T, T, K, C, f32, T, L, vp, sz, vp]),
     "ra_ring_bwd_masked": (i32, [T, T, T, T, T, L, K, C, f32, T, T, T, vp, sz, vp]),
+    "ra_ring_fwd_noalloc": (i32, [T, T, T, K, C, f32, T, L, vp]),
     "ra_bwd_ds_bytes": (sz, [T, T]),
     "ra_bwd_chunk_dkdv_ds": (i32, [T, T, T, T, L, L, K, f32, T, T, i32, vp, sz, vp]),
     "ra_bwd_chunk_dq_ds": (i32, [T, T, vp, sz, f32, T, vp]),

@@ -611,9 +611,12 @@ static ra_status check_ws(void* ws, size_t ws_bytes, size_t need) {
     return RA_OK;
 }
 
-ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
-                             const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse, void* ws,
-                             size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+ra_status check_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                         const ra_chunks* chunks, float scale, const ra_tensor* out, const ra_lse* lse) {
     RA_TRY(check_qkv(q, k, v));
     RA_TRY(check_kmask(kmask, q->B, k->S));
     RA_TRY(check_tensor(out, "out"));
@@ -621,9 +624,13 @@ ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     RA_TRY(check_rows(lse, "lse", q->B, q->H, q->S));
     RA_TRY(check_scale(scale));
     RA_TRY(check_chunks(chunks, k->S));
-    const size_t need = ra_ring_fwd_workspace_bytes(q, out);
-    RA_TRY(check_ws(ws, ws_bytes, need));
-    hipStream_t s = (hipStream_t)stream;
+    return RA_OK;
+}
+
+// The forward sweep, validated; ws holds ra_ring_fwd_workspace_bytes(q, out) bytes.
+ra_status enqueue_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                           const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse, void* ws,
+                           hipStream_t s) {
     const ra_tensor acc = out->dtype == RA_F32 ? *out : contiguous_f32(ws, *q);
     // A bf16 sweep's last non-empty step writes the final bf16 output itself (no cast pass).
     int last = -1;
@@ -638,6 +645,37 @@ ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
                                  i == last ? out : nullptr));
     }
     if (out->dtype == RA_BF16 && last < 0) RA_HIP(ra::launch_cast_f32_to_bf16(acc, *out, s));
+    return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_ring_fwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                             const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
+    RA_TRY(check_ring_fwd(q, k, v, kmask, chunks, scale, out, lse));
+    RA_TRY(check_ws(ws, ws_bytes, ra_ring_fwd_workspace_bytes(q, out)));
+    RA_TRY(enqueue_ring_fwd(q, k, v, kmask, chunks, scale, out, lse, ws, (hipStream_t)stream));
+    return ok();
+}
+
+ra_status ra_ring_fwd_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v, const ra_kmask* kmask,
+                              const ra_chunks* chunks, float scale, ra_tensor* out, ra_lse* lse, void* stream) {
+    RA_TRY(check_ring_fwd(q, k, v, kmask, chunks, scale, out, lse));
+    const size_t need = ra_ring_fwd_workspace_bytes(q, out);
+    if (need > ra::kNoAllocScratchBytes)
+        return fail(RA_E_WORKSPACE,
+                    "the sweep needs %zu bytes of scratch; ra_ring_fwd_noalloc has %zu (fp32 running output of at most "
+                    "%zu elements): use ra_ring_fwd with a workspace",
+                    need, ra::kNoAllocScratchBytes, ra::kNoAllocScratchBytes / 4);
+    void* ws = nullptr;
+    if (need > 0) {
+        size_t have = 0;
+        RA_HIP(ra::scratch_region(&ws, &have));
+    }
+    RA_TRY(enqueue_ring_fwd(q, k, v, kmask, chunks, scale, out, lse, ws, (hipStream_t)stream));
     return ok();
 }
 

@@ -36,6 +36,13 @@ inline int64_t dqs_workgroups(int B, int Hq, int Sq) {
 }
 constexpr int kMaxRanks = 16;  // exchange fan-out limit (kernel argument table)
 
+// Size of the per-GPU device array that ra_ring_fwd_noalloc uses as its workspace (the
+// fp32 running output of a bf16 sweep: 16 Mi elements, e.g. 4096 query rows x 32 heads x
+// 128).  scratch_region returns its device address on the current device (looked up
+// once per device) and its size.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t scratch_region(void** ptr, size_t* bytes);
+
 // Key mask of one chunk as the kernels see it: data[b * sB + key] != 0 means the key
 // takes part; data == nullptr means every key does.
 struct KeyMask {

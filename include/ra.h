@@ -261,6 +261,23 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
                              ra_tensor* dq, ra_tensor* dk, ra_tensor* dv,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ra_ring_fwd_masked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, validation, results and
+ * errors as ra_ring_fwd_masked (kmask may be NULL).  It allocates and frees
+ * nothing: the fp32 running output of a bf16 sweep lives in a device array of
+ * the library (64 MiB per GPU, held until the process ends), so a sweep whose
+ * ra_ring_fwd_workspace_bytes(q, out) exceeds 64 MiB (more than 16 Mi elements
+ * of q) is refused with RA_E_WORKSPACE before anything is enqueued.  The first
+ * call on a device looks the array's address up (a runtime query, no
+ * allocation; callers that capture graphs make one call before capturing).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller; calls in one stream are ordered as usual. */
+ra_status ra_ring_fwd_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
+                              const ra_kmask* kmask, const ra_chunks* chunks, float scale,
+                              ra_tensor* out, ra_lse* lse, void* stream);
+
 /* Workspace sizes.  ra_ring_fwd_workspace_bytes: what ra_ring_fwd needs.
  * ra_ring_bwd_workspace_min_bytes: ra_ring_bwd accepts any workspace of at least
  * this size with any chunk table: delta plus an fp32 accumulator for every bf16

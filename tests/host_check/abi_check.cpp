@@ -127,6 +127,23 @@ void ring_case(const Shape& s, bool masked, int grad_dt, int ws_kind) {
     void* fw = fws ? a.get(fws, "fwd ws") : nullptr;
     expect_ok(ra_ring_fwd_masked(&q, &k, &v, masked ? &m : nullptr, &ch.c, 0.0883883f, &out, &lse, fw, fws, nullptr),
               tag + " ring_fwd", s.Sq == 0);
+    {
+        hostcheck::reset();
+        Arena c;
+        const ra_tensor q3 = tensor(c, s.B, s.Sq, s.Hq, s.D, s.dt, "q", s.seq_first);
+        const ra_tensor k3 = tensor(c, s.B, s.Sk, s.Hkv, s.D, s.dt, "k", s.seq_first);
+        const ra_tensor v3 = tensor(c, s.B, s.Sk, s.Hkv, s.D, s.dt, "v", s.seq_first);
+        ra_tensor o3 = tensor(c, s.B, s.Sq, s.Hq, s.D, s.dt, "out", s.seq_first);
+        ra_lse l3 = rows(c, s.B, s.Hq, s.Sq, "lse");
+        ra_kmask m3;
+        if (masked) m3 = kmask(c, s.B, s.Sk);
+        const ra_status st = ra_ring_fwd_noalloc(&q3, &k3, &v3, masked ? &m3 : nullptr, &ch.c, 0.0883883f, &o3, &l3,
+                                                 nullptr);
+        if (fws <= (size_t(64) << 20))
+            expect_ok(st, tag + " ring_fwd_noalloc", s.Sq == 0);
+        else
+            expect_refused(st, RA_E_WORKSPACE, tag + " ring_fwd_noalloc past its scratch");
+    }
     const size_t lo = ra_ring_bwd_workspace_min_bytes(&q, &k, &dq, &dk, &dv);
     const size_t hi = ra_ring_bwd_workspace_bytes(&q, &k, &dq, &dk, &dv);
     expect(lo <= hi, tag + ": min workspace above recommended");

@@ -234,6 +234,15 @@ hipError_t launch_fill_rows(const ra_lse& t, float, hipStream_t) {
     return hipSuccess;
 }
 
+// the library's device scratch array, at a fake address registered as a buffer
+hipError_t scratch_region(void** ptr, size_t* bytes) {
+    void* const p = (void*)(uintptr_t(1) << 44);
+    add_alloc(p, kNoAllocScratchBytes, "scratch");
+    *ptr = p;
+    *bytes = kNoAllocScratchBytes;
+    return hipSuccess;
+}
+
 hipError_t launch_permute(const PermuteTable& tab, hipStream_t) {
     ++g_launches;
     for (int i = 0; i < tab.n_in; ++i) need_tensor(tab.in[i], "permute in");

@@ -94,7 +94,7 @@ struct BwdParams {
     int64_t dq_sB, dq_sS, dq_sH, dk_sB, dk_sS, dk_sH, dv_sB, dv_sS, dv_sH;
     int B, Sq, Sk, Hq, G, n_tiles;  // tiles along the kernel's stationary axis (keys or query rows)
     uint32_t q_bytes, do_bytes, k_bytes, v_bytes;
-    float scale, c;
+    float scale, c, neg_inv_scale;  // neg_inv_scale = -1 / scale
     const uint8_t* km;  // key mask of the chunk (km[b * km_sB + key] != 0: key takes part), or null
     int64_t km_sB;
     // dS workspace (bf16): one 4 KiB block per (batch, query head, 32-key group, 64-row
@@ -671,6 +671,12 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         vq[i] = copy_voff<D>(w * NI + i, lane, p.q_sS);
         vo[i] = copy_voff<D>(w * NI + i, lane, p.do_sS);
     }
+    // The tile statistics (lse, delta of its 64 rows) are loaded and staged in LDS by the
+    // first role-1 wavefront: role 1 ends its iteration with MFMAs and waits at the barrier
+    // anyway, while role 0 ends with its softmax burst (the iteration's critical path).
+    const bool stat_wave = w == kBwdWaves;
+    const int stat_row = tid - 64 * kBwdWaves;
+    static_assert(BM == 64, "one statistics row per lane of the staging wavefront");
     float lpre = 0.f, dpre = 0.f;
     // Tiles are copied in order: tile it is Q tile it % ntq of query head g G + it / ntq,
     // tracked incrementally (no division or 64-bit product per tile): each copy's source
@@ -695,9 +701,9 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
             dma16(rq, qdst + (w * NI + i) * 1024, vq[i]);
             dma16(ro, odst + (w * NI + i) * 1024, vo[i]);
         }
-        if (tid < BM) {
-            lpre = bload4f(make_rsrc(l_head + l_off, lrow_bytes - l_off), (uint32_t)tid * 4, 0);
-            dpre = bload4f(make_rsrc(d_head + l_off, lrow_bytes - l_off), (uint32_t)tid * 4, 0);
+        if (stat_wave) {
+            lpre = bload4f(make_rsrc(l_head + l_off, lrow_bytes - l_off), (uint32_t)stat_row * 4, 0);
+            dpre = bload4f(make_rsrc(d_head + l_off, lrow_bytes - l_off), (uint32_t)stat_row * 4, 0);
         }
         if (++iss_t == ntq) {
             iss_t = 0;
@@ -713,12 +719,13 @@ __global__ __launch_bounds__(64 * kBwdWaves * 2) void bwd_kv_bf16_kernel(BwdPara
         }
     };
     auto commit_stats = [&](int buf) {
-        if (tid < BM) {
+        if (stat_wave) {
             // role 0 starts its S accumulator at -lse / scale, role 1 its dP accumulator at
-            // -delta (scale > 0 and >= 2^-100 is checked on the host, so -lse / scale is finite
-            // for every finite lse)
-            stat[(2 * buf) * BM + tid] = -lpre / p.scale;
-            stat[(2 * buf + 1) * BM + tid] = -dpre;
+            // -delta (scale >= 2^-100 is checked on the host, so -lse / scale is finite for
+            // every finite lse; the product with the reciprocal differs from the quotient by
+            // at most one rounding, 2^-24 relative)
+            stat[(2 * buf) * BM + stat_row] = lpre * p.neg_inv_scale;
+            stat[(2 * buf + 1) * BM + stat_row] = -dpre;
         }
     };
 
@@ -1438,6 +1445,7 @@ BwdParams bwd_params(const ra_tensor& q, const ra_tensor& k, const ra_tensor& v,
     p.v_bytes = span_bytes(v.S, v.sS, v.D);
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
+    p.neg_inv_scale = (float)(-1.0 / (double)scale);
     p.km = nullptr;
     p.km_sB = 0;
     p.ds = nullptr;

@@ -52,6 +52,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef RA_LDS uint16_t lds_u16;
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold of the running max, in log2 units
+constexpr int kFwdStageB = 32 * 128;  // forward output staging per wavefront: 32 rows x one 128-byte line
 
 // f(std::integral_constant<int, I>) for I = B .. E - 1, as straight-line code (the
 // indices are compile-time constants inside f).
@@ -242,6 +243,8 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     static_assert(RC >= 8 && NI >= 1, "tile geometry");
     __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];   // [K0 | V0 | K1 | V1]
     RA_LDS char* const lbase = (RA_LDS char*)smem;
+    // output staging of the epilogue, 4 KiB per wavefront (32 rows x 32 fp32 columns)
+    __shared__ __attribute__((aligned(16))) char ostage[kFwdWaves * kFwdStageB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     // key; the highest hit of the workgroup's wavefronts bounds the sweep.
     int sk_eff = p.Sk;
     if constexpr (MASK) {
-        __shared__ int last_valid[kFwdWaves];
+        RA_LDS int* const last_valid = (RA_LDS int*)ostage;  // free until the epilogue
         int last = -1;
         for (int t0 = ntiles_all - 1 - w; t0 >= 0 && last < 0; t0 -= 4 * kFwdWaves) {
             uint32_t kb4[4];
@@ -533,67 +536,98 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     }
 
     l = half_sum(l);
-    if (!row_ok) return;
-    float* orow = p.out + (int64_t)b * p.o_sB + (int64_t)row * p.o_sS + (int64_t)h * p.o_sH;
+    // Epilogue.  Row r of the result is wa(r) * (running output) + wc(r) * oacc (wa = 0 when
+    // the step starts the running state).  A lane holds 4-column pieces of its one row, so
+    // storing straight from the accumulators would write 32 rows x 32 bytes per instruction
+    // and leave lines of the row-strided output partly written in between (the counters
+    // then see up to twice the output's bytes written).
     float* lp = p.lse + (int64_t)b * p.l_sB + (int64_t)h * p.l_sH + row;
+    float wa = 0.f, wc = 0.f, lse_new = -INFINITY;
+    bool lse_keep = false;  // the running LSE stays as it is
+    if (MASK && l == 0.f) {
+        // every key of the chunk masked for this row: the step's partial is the merge
+        // identity (a merge keeps the running state; a first step writes 0 and LSE -inf)
+        if (MERGE) {
+            wa = 1.f;
+            lse_keep = true;
+        }
+    } else {
+        const float inv_l = 1.f / l;
+        const float lse_c = m * kLn2 + logf(l);
+        if (!MERGE) {
+            wc = inv_l;
+            lse_new = lse_c;
+        } else {
+            // both lanes of the row (l and l^32) read lse_acc before lane l writes it
+            const float la = row_ok ? *lp : 0.f;
+            const float mm = fmaxf(la, lse_c);
+            const float ea = expf(la - mm), ec = expf(lse_c - mm);
+            const float sum = ea + ec;
+            wa = ea / sum;
+            wc = ec / sum * inv_l;
+            lse_new = mm + logf(sum);
+        }
+    }
+    // Each wavefront passes wc * oacc through its own 4 KiB of LDS, 32 columns (one
+    // 128-byte line per row) at a time, and stores whole lines: 8 rows per instruction.
+    // Branch-free but for the stores, so that the loads of the running output all issue
+    // up front (a row past the end reads row Sq - 1 and stores nothing).
+    RA_LDS char* const ost = (RA_LDS char*)ostage + w * kFwdStageB;
+    const int rsub = lane >> 3, cc = lane & 7;  // writer lane: row 8 k + rsub, 16-byte chunk cc
+    const int row0 = qt * BM + w * 32;
+    float* const obase = p.out + (int64_t)b * p.o_sB + (int64_t)h * p.o_sH + 4 * cc;
     // the output of the sweep's last step goes straight to the final bf16 tensor (rounded to
     // nearest even, as the cast it replaces would)
-    uint16_t* o16row = p.out16 ? p.out16 + (int64_t)b * p.o16_sB + (int64_t)row * p.o16_sS + (int64_t)h * p.o16_sH
-                               : nullptr;
-    auto put = [&](int db, int g4, const f32x4_t& v4) {
-        if (o16row)
-            *(u32x2_t*)(o16row + 32 * db + 8 * g4 + 4 * hh) = u32x2_t{pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-        else
-            *(f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh) = v4;
-    };
-    if (MASK && l == 0.f) {
-        // every key of the chunk masked: the step's partial is the merge identity (a merge
-        // leaves the running state as it is; only a final bf16 output must still be written)
-        if (!MERGE) {
+    uint16_t* const o16base = p.out16 ? p.out16 + (int64_t)b * p.o16_sB + (int64_t)h * p.o16_sH + 4 * cc : nullptr;
+    float wa_r[4];  // wa of the rows this lane writes (lane r < 32 holds row r)
+    f32x4_t old[MERGE ? DB : 1][4];
+    if constexpr (MERGE) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int k = 0; k < 4; ++k) {
+            wa_r[k] = __shfl(wa, 8 * k + rsub);
+            const int64_t grow = min(row0 + 8 * k + rsub, p.Sq - 1);
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) put(db, g4, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            if (hh == 0) *lp = -INFINITY;
-        } else if (o16row) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) put(db, g4, *(const f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh));
+            for (int db = 0; db < DB; ++db) old[db][k] = *(const f32x4_t*)(obase + grow * p.o_sS + 32 * db);
         }
-        return;
     }
-    const float inv_l = 1.f / l;
-    const float lse_c = m * kLn2 + logf(l);
-    if (!MERGE) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+        // chunk 2 g4 + hh of row l32 (columns 32 db + 8 g4 + 4 hh .. + 3), XOR-swizzled by
+        // row pairs so that 16 consecutive lanes hit distinct banks on both sides
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4_t v4 = {oacc[db][4 * g4] * inv_l, oacc[db][4 * g4 + 1] * inv_l,
-                                    oacc[db][4 * g4 + 2] * inv_l, oacc[db][4 * g4 + 3] * inv_l};
-                put(db, g4, v4);
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4_t v4 = {wc * oacc[db][4 * g4], wc * oacc[db][4 * g4 + 1], wc * oacc[db][4 * g4 + 2],
+                                wc * oacc[db][4 * g4 + 3]};
+            *(RA_LDS f32x4_t*)(ost + l32 * 128 + 16 * ((2 * g4 + hh) ^ ((l32 >> 1) & 7))) = v4;
+        }
+        // LDS runs one wavefront's accesses in order: a compiler barrier suffices
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t v4[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int rr = 8 * k + rsub;
+            v4[k] = *(const RA_LDS f32x4_t*)(ost + rr * 128 + 16 * (cc ^ ((rr >> 1) & 7)));
+        }
+        asm volatile("" ::: "memory");  // the next quarter's staging stays behind these reads
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int grow = row0 + 8 * k + rsub;
+            if constexpr (MERGE) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v4[k][j] += wa_r[k] == 0.f ? 0.f : wa_r[k] * old[db][k][j];
             }
-        if (hh == 0) *lp = lse_c;
-    } else {
-        // both lanes of the row (l and l^32) read lse_acc before lane l writes it (same wavefront)
-        const float la = *lp;
-        const float mm = fmaxf(la, lse_c);
-        const float ea = expf(la - mm), ec = expf(lse_c - mm);
-        const float sum = ea + ec;
-        const float wa = ea / sum, wc = ec / sum * inv_l;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4_t old = *(const f32x4_t*)(orow + 32 * db + 8 * g4 + 4 * hh);
-                f32x4_t v4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v4[j] = (wa == 0.f ? 0.f : wa * old[j]) + wc * oacc[db][4 * g4 + j];
-                put(db, g4, v4);
+            if (grow < p.Sq) {
+                if (o16base)
+                    *(u32x2_t*)(o16base + (int64_t)grow * p.o16_sS + 32 * db) =
+                        u32x2_t{pack_bf16x2(v4[k][0], v4[k][1]), pack_bf16x2(v4[k][2], v4[k][3])};
+                else
+                    *(f32x4_t*)(obase + (int64_t)grow * p.o_sS + 32 * db) = v4[k];
             }
-        if (hh == 0) *lp = mm + logf(sum);
+        }
     }
+    if (row_ok && hh == 0 && !lse_keep) *lp = lse_new;
 }
 
 // ============================================================================ backward

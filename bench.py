@@ -10,8 +10,9 @@ steps, merges, finalisation casts).
 Prints ONE JSON line.  ``value`` is fwd+bwd TFLOP/s with the attention flop
 count 4*B*Hq*Sq*Sk*D (forward) + 10*B*Hq*Sq*Sk*D (backward, five products
 including the recompute).  ``roofline`` describes the dominant kernel (the
-dK/dV kernel of the backward chunk step), timed per launch with HIP events on
-the stream it runs on, each launch placed as in the backward sweep;
+dK/dV kernel of the backward chunk step): the backward sweep's 8 launches,
+issued as in the sweep right after a forward sweep, timed with HIP events on
+the stream they run on;
 ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
 workload on the host cores.
 """
@@ -30,7 +31,7 @@ import context_attention_lse_kv_amd as ra  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 bf16 flop/clk/CU (dense MFMA)
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "ring attn fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 
 
@@ -106,8 +107,8 @@ def run_workload(full, steps, warmup, masked=False, single=False):
     t_bwd = timed(bwd, max(3, steps // 2), 1)
     f_f, f_b = flops(w.B, w.Hq, q.shape[1], w.S, w.D)
     return dict(w=w, lens=lens, order=order, q=q, k=k, v=v, do=do, out=out, lse=lse, dq=dq, dk=dk, dv=dv,
-                t_step=t_step, t_fwd=t_fwd, t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step, bwd=bwd,
-                step_ms=step_ms)
+                t_step=t_step, t_fwd=t_fwd, t_bwd=t_bwd, f_f=f_f, f_b=f_b, km=km, step=step, fwd=fwd, bwd=bwd,
+                bws=bws, step_ms=step_ms)
 
 
 def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
@@ -118,13 +119,15 @@ def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
 
     The ring backward of the shard runs its 8 dK/dV launches back to back (their dS go
     to consecutive parts of the dS region; one dQ pass over all of them follows), so the
-    timed launches run back to back too, each between a HIP event pair on the stream;
-    the result is the mean of the per-launch event intervals.  The board's clock settles
-    only under sustained load (after an idle gap it boosts, overshoots its power limit
-    and throttles for a few milliseconds), so `lead_steps` whole ring steps are queued
-    right before the timed launches, with no host synchronisation in between.
+    timed launches run back to back too, between one HIP event pair on the stream (no
+    event between them, as in the ring); the result is the interval over the number of
+    launches.  The board's clock settles only under sustained load (after an idle gap it
+    boosts, overshoots its power limit and throttles for a few milliseconds), so
+    `lead_steps` whole ring steps are queued right before the timed launches, with no
+    host synchronisation in between.
     `back_to_back=False` puts a dQ pass of the same chunk before each timed launch
-    instead (the order of the per-chunk entry points)."""
+    instead (the order of the per-chunk entry points), each launch between its own event
+    pair."""
     q, k, v, do, out, lse = r["q"], r["k"], r["v"], r["do"], r["out"], r["lse"]
     c = r["lens"][0]
     kc, vc = k[:, :c], v[:, :c]
@@ -142,9 +145,15 @@ def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
     torch.cuda.synchronize()
     for _ in range(lead_steps):
         r["step"]()
+    if back_to_back:
+        ev[0][0].record(s)
+        for _ in range(launches):
+            ra.bwd_chunk_dkdv_ds(q, kc, vc, do, lse, delta, dk, dv, 0, ds)
+        ev[0][1].record(s)
+        torch.cuda.synchronize()
+        return ev[0][0].elapsed_time(ev[0][1]) / launches / 1e3, f
     for i in range(launches):
-        if not back_to_back:
-            ra.bwd_chunk_dq_ds(q, kc, ds, dq)
+        ra.bwd_chunk_dq_ds(q, kc, ds, dq)
         ev[i][0].record(s)
         ra.bwd_chunk_dkdv_ds(q, kc, vc, do, lse, delta, dk, dv, 0, ds)
         ev[i][1].record(s)
@@ -157,9 +166,10 @@ def forward_kernel(r, lead_steps=3):
     """The forward chunk step as the ring sweep runs it after its first step: one launch of
     fwd_bf16_kernel<128, MERGE> per chunk, each merging its partial into the running fp32
     (output, LSE) state in its epilogue.  The shard's 7 merging launches (chunks in ring
-    order after the local one) run back to back, each between a HIP event pair on the
-    stream, after `lead_steps` whole ring steps queued without a host synchronisation
-    (the clock settles only under sustained load).  4*D flop per (query row, key, head)."""
+    order after the local one) run back to back between one HIP event pair on the stream,
+    after `lead_steps` whole ring steps queued without a host synchronisation (the clock
+    settles only under sustained load); the result is the interval over the number of
+    launches.  4*D flop per (query row, key, head)."""
     q, k, v = r["q"], r["k"], r["v"]
     lens, order = r["lens"], r["order"]
     starts = [sum(lens[:i]) for i in range(len(lens))]
@@ -169,35 +179,65 @@ def forward_kernel(r, lead_steps=3):
     ra.fwd_chunk(q, k[:, starts[c0]:starts[c0] + lens[c0]], v[:, starts[c0]:starts[c0] + lens[c0]], acc, lse, merge=0)
     s = torch.cuda.current_stream()
     rest = order[1:]
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in rest]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     for _ in range(lead_steps):
         r["step"]()
-    for (a, b), c in zip(ev, rest):
-        a.record(s)
+    a.record(s)
+    for c in rest:
         ra.fwd_chunk(q, k[:, starts[c]:starts[c] + lens[c]], v[:, starts[c]:starts[c] + lens[c]], acc, lse, merge=1)
-        b.record(s)
+    b.record(s)
     torch.cuda.synchronize()
-    t = sum(a.elapsed_time(b) for a, b in ev) / len(ev) / 1e3
+    t = a.elapsed_time(b) / len(rest) / 1e3
     w = r["w"]
     return t, 4.0 * w.B * w.Hq * q.shape[1] * lens[rest[0]] * w.D
 
 
-def backward_sweep_events(r, reps=6, lead_steps=2):
-    """Median HIP-event duration (s) of one ring backward sweep of the shard, each sweep
-    between an event pair, after `lead_steps` whole ring steps."""
+def backward_windows(r, reps=4):
+    """HIP-event timing of the shard's backward sweep and of its parts, each rep right
+    after a forward sweep, as in the step.  Rep i times (a) the whole ring backward sweep
+    (one library call: delta, the 8 dK/dV launches, the dQ pass over all 8 chunks' dS),
+    then, after another forward sweep, (b) the same sweep's delta and 8 dK/dV launches
+    issued through the per-chunk entry points: the chunks in ring order, each writing its
+    final bf16 dK/dV rows and its dS into consecutive parts of the sweep's dS region.
+    Returns medians in seconds: the sweep, delta + the 8 dK/dV launches, and the mean
+    dK/dV launch (the 8 launches back to back between one event pair)."""
+    q, k, v, do, out, lse = r["q"], r["k"], r["v"], r["do"], r["out"], r["lse"]
+    lens, order, bws = r["lens"], r["order"], r["bws"]
+    starts = [sum(lens[:i]) for i in range(len(lens))]
+    delta = torch.empty_like(lse)
+    dk, dv = r["dk"], r["dv"]
+    off = (lse.numel() * 4 + 255) // 256 * 256  # the sweep's delta rows come first in its workspace
+    ds_parts = []
+    for c in order:
+        n = ra.bwd_ds_bytes(q, k[:, starts[c]:starts[c] + lens[c]])
+        ds_parts.append(bws[off:off + n])
+        off += n
     s = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    sweeps, parts, kvs = [], [], []
     torch.cuda.synchronize()
-    for _ in range(lead_steps):
-        r["step"]()
-    for a, b in ev:
+    for _ in range(reps):
+        r["fwd"]()
+        a, b = mk(), mk()
         a.record(s)
         r["bwd"]()
         b.record(s)
-    torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in ev)
-    return ts[len(ts) // 2] / 1e3
+        r["fwd"]()
+        e0, e1, e2 = mk(), mk(), mk()
+        e0.record(s)
+        ra.bwd_delta(out, do, delta)
+        e1.record(s)
+        for c, ds in zip(order, ds_parts):
+            sl = slice(starts[c], starts[c] + lens[c])
+            ra.bwd_chunk_dkdv_ds(q, k[:, sl], v[:, sl], do, lse, delta, dk[:, sl], dv[:, sl], 0, ds)
+        e2.record(s)
+        torch.cuda.synchronize()
+        sweeps.append(a.elapsed_time(b))
+        parts.append(e0.elapsed_time(e2))
+        kvs.append(e1.elapsed_time(e2) / len(order))
+    med = lambda xs: sorted(xs)[len(xs) // 2] / 1e3
+    return med(sweeps), med(parts), med(kvs)
 
 
 def image_dit_fwd(steps=20, warmup=3):
@@ -225,7 +265,6 @@ def image_dit_fwd(steps=20, warmup=3):
                                        "pct_of_peak": round(100.0 * f / t1 / 1e12 / PEAK_BF16_TFLOPS, 2)}}
 
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 
 
 def hbm_kernels(r, reps=10):
@@ -302,6 +341,21 @@ def roofline_entry(kernel, flop, seconds, method_bytes, profile, note=None):
          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(seconds * 1e3, 4),
          "method_flop": flop, "method_bytes": int(method_bytes), "traffic": traffic,
          "traffic_ratio": None if traffic is None else round(traffic / method_bytes, 2)}
+    if note:
+        e["note"] = note
+    return e
+
+
+def hbm_roofline_entry(kernel, nbytes, seconds, flop, profile, note=None):
+    """One HBM-bound kernel against the HBM peak: `nbytes` = the bytes its algorithm moves
+    per launch (each input byte read once, each output byte written once), `traffic` the
+    counters' figure for it, as in roofline_entry."""
+    gbps = nbytes / seconds / 1e9
+    traffic = measured_traffic(profile)
+    e = {"bound": "hbm", "kernel": kernel, "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_ms": round(seconds * 1e3, 4), "bytes": int(nbytes),
+         "flop": flop, "tflops": round(flop / seconds / 1e12, 2), "traffic": traffic,
+         "traffic_ratio": None if traffic is None else round(traffic / nbytes, 3)}
     if note:
         e["note"] = note
     return e
@@ -439,10 +493,10 @@ def main():
     n_ch = len(r["lens"])
     # the method's HBM bytes per launch: inputs read once, outputs written once (bf16 = 2 B, fp32 = 4 B)
     q_b, kv_b, st_b = B * Sq * Hq * D * 2, B * Sc * Hkv * D * 2, B * Hq * Sq * 4
-    t_k, f_k = dominant_kernel(r)
+    f_k = 8.0 * B * Hq * Sq * Sc * D
+    t_bwd_ev, t_delta_kv, t_k = backward_windows(r)
     t_after_dq, _ = dominant_kernel(r, back_to_back=False)
     t_f, f_f1 = forward_kernel(r)
-    t_bwd_ev = backward_sweep_events(r)
     snap = None if args.no_cpu_baseline else snapshot(r)
     dkdv = roofline_entry(
         "bwd_kv_bf16_kernel<128> (dK/dV of one ring step, storing dS: 4096 q rows x 4096 keys x 32 heads)",
@@ -455,14 +509,16 @@ def main():
         f_f1, t_f, q_b + 2 * kv_b + 2 * (2 * q_b + st_b), "fwd_bf16_video_dit_shard.md",
         note="method bytes: Q, K_j, V_j read; the running fp32 output and LSE read and written (the LSE merge)")
     # the dQ pass: one launch per backward sweep over the dS of all chunks; its time is the sweep's
-    # HIP-event time minus its 8 dK/dV launches (back to back, as above) and delta (hbm_kernels)
+    # HIP-event time minus the same sweep's delta and 8 dK/dV launches (backward_windows)
     res_hbm = hbm_kernels(r)
-    t_dq = t_bwd_ev - n_ch * t_k - res_hbm["bwd_delta"]["ms"] / 1e3
-    dqp = roofline_entry(
+    t_dq = t_bwd_ev - t_delta_kv
+    ds_b = n_ch * B * Hq * Sq * Sc * 2  # the stored dS of every chunk (bf16)
+    dqp = hbm_roofline_entry(
         "bwd_dqs_bf16_kernel<128> (dQ of the whole backward sweep from the stored dS of its 8 chunks)",
-        2.0 * B * Hq * Sq * w.S * D, t_dq, n_ch * kv_b + q_b, "bwd_dqs_bf16_video_dit_shard.md",
-        note="time derived: backward sweep (HIP events) minus its dK/dV launches and delta; method bytes: K of "
-             "every chunk read, dq (bf16) written.  The route also reads the stored dS (8 GiB per sweep)")
+        ds_b + n_ch * kv_b + q_b, t_dq, 2.0 * B * Hq * Sq * w.S * D, "bwd_dqs_bf16_video_dit_shard.md",
+        note="time derived: backward sweep (HIP events) minus the same sweep's delta and dK/dV launches "
+             "(issued through the per-chunk entry points); bytes: the stored dS and K of every chunk read, "
+             "dq (bf16) written")
     res = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -592,13 +592,14 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        // chunk 2 g4 + hh of row l32 (columns 32 db + 8 g4 + 4 hh .. + 3), XOR-swizzled by
-        // row pairs so that 16 consecutive lanes hit distinct banks on both sides
+        // chunk 2 g4 + hh of row l32 (columns 32 db + 8 g4 + 4 hh .. + 3), XOR-swizzled by the
+        // row's low 3 bits: the 8 lanes of one 128-byte LDS access (8 rows here, 8 chunks
+        // of one row when read back) hit 8 distinct chunk positions
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const f32x4_t v4 = {wc * oacc[db][4 * g4], wc * oacc[db][4 * g4 + 1], wc * oacc[db][4 * g4 + 2],
                                 wc * oacc[db][4 * g4 + 3]};
-            *(RA_LDS f32x4_t*)(ost + l32 * 128 + 16 * ((2 * g4 + hh) ^ ((l32 >> 1) & 7))) = v4;
+            *(RA_LDS f32x4_t*)(ost + l32 * 128 + 16 * ((2 * g4 + hh) ^ (l32 & 7))) = v4;
         }
         // LDS runs one wavefront's accesses in order: a compiler barrier suffices
         asm volatile("" ::: "memory");
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(64 * kFwdWaves, 2) void fwd_bf16_kernel(FwdParams p
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int rr = 8 * k + rsub;
-            v4[k] = *(const RA_LDS f32x4_t*)(ost + rr * 128 + 16 * (cc ^ ((rr >> 1) & 7)));
+            v4[k] = *(const RA_LDS f32x4_t*)(ost + rr * 128 + 16 * (cc ^ (rr & 7)));
         }
         asm volatile("" ::: "memory");  // the next quarter's staging stays behind these reads
         __builtin_amdgcn_sched_barrier(0);

@@ -429,6 +429,41 @@ def test_edge_cases():
     check_bf16('out', np64(out), ref_o)
 
 
+def _strided_like(t, row_stride):
+    """A device view of `t` ([1, S, H, D]) whose rows lie `row_stride` elements apart in one
+    large buffer (heads adjacent within a row); the gaps between rows are never read."""
+    _, S, H, D = t.shape
+    buf = torch.empty((S - 1) * row_stride + H * D, dtype=t.dtype, device=dev())
+    view = buf.as_strided((1, S, H, D), (S * row_stride, row_stride, D, 1))
+    view.copy_(t.to(dev()))
+    return view
+
+
+@pytest.mark.parametrize("grad_dtype", [torch.bfloat16, torch.float32])
+def test_largest_accepted_slice_span(grad_dtype):
+    """q, k, v, dout whose (batch, head) slices span just under 2^31 bytes (the largest the
+    bf16 kernels' 32-bit buffer offsets accept, tile slack included): ragged tiles, GQA, two
+    chunks, against the oracle."""
+    Sq, Sk, Hq, Hkv, D = 200, 300, 2, 1, 128
+    q = W.randn((1, Sq, Hq, D), 41, "bf16"); k = W.randn((1, Sk, Hkv, D), 42, "bf16")
+    v = W.randn((1, Sk, Hkv, D), 43, "bf16"); do = W.randn((1, Sq, Hq, D), 44, "bf16")
+    # largest row strides (multiples of 8 elements) with ((S + 128) * sS + D) * 2 < 2^31
+    sq = ((2**30 - D) // (Sq + 128)) // 8 * 8
+    sk = ((2**30 - D) // (Sk + 128)) // 8 * 8
+    for S, st in ((Sq, sq), (Sk, sk)):
+        span = ((S + 128) * st + D) * 2
+        assert 2**31 - 2 * (S + 128) * 16 < span < 2**31
+    gq, gdo = _strided_like(q, sq), _strided_like(do, sq)
+    gk, gv = _strided_like(k, sk), _strided_like(v, sk)
+    ref_o, ref_l = oracle.attention_forward(np64(q), np64(k), np64(v))
+    ref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(do))
+    out, lse, dq, dk, dv = ring(gq, gk, gv, gdo, [150, 150], [1, 0], grad_dtype=grad_dtype)
+    check_bf16('out', np64(out), ref_o)
+    assert max_abs(np64(lse), ref_l) <= LSE_TOL_BF16
+    for name, got, r in zip(('dq', 'dk', 'dv'), (dq, dk, dv), ref):
+        check_bf16(name, np64(got), r)
+
+
 def test_fp32_path_d128_gqa():
     B, Sq, Sk, Hq, Hkv, D = 1, 45, 130, 4, 2, 128
     q = W.randn((B, Sq, Hq, D), 14); k = W.randn((B, Sk, Hkv, D), 15); v = W.randn((B, Sk, Hkv, D), 16)

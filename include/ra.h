@@ -22,11 +22,15 @@
  * Memory: every pointer in a tensor descriptor is DEVICE memory owned by the
  *   caller; the library never allocates or frees device memory.  Host arrays
  *   (chunk tables, tensor arrays, size outputs) are read/written during the
- *   call only.  Scratch space is passed in as a caller-owned workspace.
+ *   call only.  Scratch space is passed in as a caller-owned workspace (except
+ *   for ra_ring_fwd_noalloc, which uses a device array of the library itself).
  * Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
  *   work and return without synchronising; pointers must stay valid until the
  *   enqueued work completes.  The library keeps no global state beyond a
- *   thread-local error string, so it is thread-safe.
+ *   thread-local error string and, for ra_ring_fwd_noalloc, that device array
+ *   and its per-device address (looked up once, under a lock), so every entry
+ *   point is thread-safe; concurrent ra_ring_fwd_noalloc calls on one GPU
+ *   share its array (see there).
  * Layout: an ra_tensor is a logical [B, S, H, D] tensor with element strides
  *   sB, sS, sH and D contiguous (stride 1).  Batch-first [B,S,H,D] ([P1]
  *   "Reproduction") and sequence-first [S,B,H,D] ([P4] "Testcase") are the same

@@ -23,7 +23,7 @@ EXPORTS = [
     "ra_ring_fwd_masked", "ra_ring_bwd_masked", "ra_ring_fwd_noalloc",
     "ra_bwd_ds_bytes", "ra_bwd_chunk_dkdv_ds", "ra_bwd_chunk_dq_ds",
     "ra_ring_fwd_workspace_bytes", "ra_ring_bwd_workspace_bytes", "ra_ring_bwd_workspace_min_bytes",
-    "ra_seq_head_permute",
+    "ra_ring_bwd_plan", "ra_seq_head_permute",
     "ra_split_sizes", "ra_ring_order", "ra_status_string", "ra_last_error", "ra_version",
 ]
 
@@ -77,6 +77,7 @@ _SIGS = {
     "ra_ring_fwd_workspace_bytes": (sz, [T, T]),
     "ra_ring_bwd_workspace_bytes": (sz, [T, T, T, T, T]),
     "ra_ring_bwd_workspace_min_bytes": (sz, [T, T, T, T, T]),
+    "ra_ring_bwd_plan": (i32, [T, T, T, T, T, C, sz, I32P, I32P, ctypes.POINTER(ctypes.c_uint32)]),
     "ra_seq_head_permute": (i32, [T, i32, T, i32, i32, vp]),
     "ra_split_sizes": (i32, [i32, i32, I32P]),
     "ra_ring_order": (i32, [i32, i32, I32P]),

@@ -482,6 +482,10 @@ static constexpr int64_t kDsBudget = int64_t(8) << 30;
 // a sliced chunk keeps the stored-dS route only while each slice's dQ pass has at least
 // this many workgroups (one per compute unit)
 static constexpr int64_t kMinSliceWorkgroups = 256;
+// the sweep runs slice-major (every chunk's dK/dV on a slice of query rows, then one dQ
+// pass over all of them) only with slices of at least this many rows: each dK/dV
+// launch then still sweeps as many rows as the video shard's
+static constexpr int64_t kMinGroupRows = 4096;
 
 static size_t ds_region_bytes(const ra_tensor& q, const ra_tensor& k) {
     if (q.dtype != RA_BF16 || q.S == 0 || k.S == 0) return 0;
@@ -493,20 +497,27 @@ static size_t ds_region_bytes(const ra_tensor& q, const ra_tensor& k) {
 
 namespace {
 
-// Plan of the ring backward for a given workspace size.  Per chunk (in sweep order), the
-// stored-dS route with query slices of `rows` rows, or the recompute route (rows = 0).
+// Plan of the ring backward for a given workspace size.  Chunk-major (the default): per
+// chunk (in sweep order), the stored-dS route with query slices of `rows` rows, or the
+// recompute route (rows = 0).  Slice-major (slice_rows > 0), when the dS of every chunk
+// does not fit at once but that of every chunk for a slice of at least kMinGroupRows
+// query rows does: each slice runs the dK/dV launches of all chunks, in sweep order, and
+// then one dQ pass over their dS that writes the slice's dq rows once (no fp32 dQ
+// accumulator read and written per chunk, which costs the chunk-major sweep more than the
+// slice-major one's dK/dV accumulation over slices).
 // fp32 accumulators are carved from the workspace only for bf16 gradients that need one:
 // dK/dV when some chunk is swept in more than one slice (else each chunk's rows are final
 // after its one dK/dV launch and are written in bf16 directly), dQ unless one dQ pass
-// covers the dS of every chunk (it then writes the bf16 dq directly).
+// covers the dS of every chunk for the rows it writes (it then writes the bf16 dq directly).
 struct BwdStep {
     int c;
     int32_t rows;
 };
 struct BwdPlan {
     std::vector<BwdStep> steps;
-    bool single = false;     // every chunk in one slice on the stored-dS route
+    bool single = false;     // chunk-major, every chunk in one slice on the stored-dS route
     bool one_group = false;  // ... and one dQ pass covers all of them
+    int32_t slice_rows = 0;  // > 0: slice-major with slices of this many query rows
     bool dq_acc = false, dk_acc = false, dv_acc = false;
     size_t delta_b = 0, dq_b = 0, dk_b = 0, dv_b = 0;
     size_t fixed() const {
@@ -532,6 +543,19 @@ void plan_steps(BwdPlan& P, const ra_tensor& q, const ra_chunks& ch, int64_t ds_
     int64_t all = 0;
     for (const BwdStep& st : P.steps) all += (int64_t)round256((size_t)ra::ds_bytes(q.B, q.H, q.S, ch.len[st.c]));
     P.one_group = P.single && P.steps.size() <= (size_t)ra::kDqsMaxChunks && all <= ds_room;
+    P.slice_rows = 0;
+    if (P.one_group || P.steps.empty() || P.steps.size() > (size_t)ra::kDqsMaxChunks) return;
+    int64_t per64 = 0, slab = q.S;  // dS of 64 rows against every chunk; 32-bit slab bound
+    for (const BwdStep& st : P.steps) {
+        if (st.rows == 0) return;  // a chunk on the recompute route
+        per64 += ra::ds_bytes(q.B, q.H, 64, ch.len[st.c]);
+        slab = std::min<int64_t>(slab, 64 * ((int64_t(1) << 31) / ra::ds_bytes(1, 1, 64, ch.len[st.c])));
+    }
+    const int64_t rows = std::min<int64_t>(64 * (ds_room / per64), slab);
+    if (rows >= kMinGroupRows && rows < q.S) {
+        P.slice_rows = (int32_t)rows;
+        P.single = false;
+    }
 }
 
 // The plan for a workspace of ws_bytes (SIZE_MAX: the recommended size, with a dS region
@@ -549,7 +573,7 @@ BwdPlan plan_bwd(const ra_tensor& q, const ra_tensor& k, const ra_chunks& ch, co
         const int64_t room = rec ? (int64_t)ds_region_bytes(q, k)
                                  : (ws_bytes > f ? (int64_t)((ws_bytes - f) & ~(size_t)255) : 0);
         plan_steps(P, q, ch, room);
-        const bool ndq = dq.dtype == RA_BF16 && !P.one_group;
+        const bool ndq = dq.dtype == RA_BF16 && !P.one_group && P.slice_rows == 0;
         const bool nkv = !(P.single && dk.dtype == RA_BF16 && dv.dtype == RA_BF16);
         const bool ndk = dk.dtype == RA_BF16 && nkv, ndv = dv.dtype == RA_BF16 && nkv;
         if ((!ndq || P.dq_acc) && (!ndk || P.dk_acc) && (!ndv || P.dv_acc)) break;
@@ -593,6 +617,28 @@ size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const
     // never below the size any chunk table is accepted with (a table whose plan needs
     // every accumulator then still runs; accumulators its plan skips become dS room)
     return std::max(P.fixed() + ds_region_bytes(*q, *k), ra_ring_bwd_workspace_min_bytes(q, k, dq, dk, dv));
+}
+
+ra_status ra_ring_bwd_plan(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq, const ra_tensor* dk,
+                           const ra_tensor* dv, const ra_chunks* chunks, size_t ws_bytes, int32_t* slice_rows,
+                           int32_t* rows, uint32_t* accs) {
+    RA_TRY(check_tensor(q, "q"));
+    RA_TRY(check_tensor(k, "k"));
+    RA_TRY(check_chunks(chunks, k->S));
+    const ra_tensor dq_ = dq ? *dq : *q, dk_ = dk ? *dk : *k, dv_ = dv ? *dv : *k;
+    for (const ra_tensor* t : {&dq_, &dk_, &dv_})
+        if (esize(t->dtype) == 0) return fail(RA_E_DTYPE, "gradient dtype %d is neither RA_BF16 nor RA_F32", t->dtype);
+    const BwdPlan P = plan_bwd(*q, *k, *chunks, dq_, dk_, dv_, ws_bytes);
+    if (ws_bytes < P.fixed())
+        return fail(RA_E_WORKSPACE, "workspace of %zu bytes needed, got %zu", P.fixed(), ws_bytes);
+    if (slice_rows) *slice_rows = P.slice_rows;
+    if (rows) {
+        std::vector<int32_t> by_chunk((size_t)chunks->n, -1);
+        for (const BwdStep& st : P.steps) by_chunk[(size_t)st.c] = st.rows > 0 && P.slice_rows > 0 ? P.slice_rows : st.rows;
+        for (int i = 0; i < chunks->n; ++i) rows[i] = by_chunk[(size_t)chunks->order[i]];
+    }
+    if (accs) *accs = (P.dq_acc ? 1u : 0u) | (P.dk_acc ? 2u : 0u) | (P.dv_acc ? 4u : 0u);
+    return ok();
 }
 
 
@@ -718,16 +764,44 @@ ra_status ra_ring_bwd_masked(const ra_tensor* q, const ra_tensor* k, const ra_te
     const int64_t ds_room = ws_bytes > P.fixed() ? (int64_t)((ws_bytes - P.fixed()) & ~(size_t)255) : 0;
     const std::vector<BwdStep>& steps = P.steps;
     const bool single = P.single;
+    const int32_t slice_rows = P.slice_rows;
     const bool direct_kv = single && dk->dtype == RA_BF16 && dv->dtype == RA_BF16;
-    const bool direct_dq = single && dq->dtype == RA_BF16;
+    const bool direct_dq = (single || slice_rows > 0) && dq->dtype == RA_BF16;
 
     RA_HIP(ra::launch_bwd_delta(*out, *dout, delta, s));
-    if (!direct_dq) RA_HIP(ra::launch_zero_f32(dq_acc, s));
+    // slice-major: each slice's one dQ pass writes its rows without reading them
+    if (!direct_dq && slice_rows == 0) RA_HIP(ra::launch_zero_f32(dq_acc, s));
     if (!direct_kv) {
         RA_HIP(ra::launch_zero_f32(dk_acc, s));
         RA_HIP(ra::launch_zero_f32(dv_acc, s));
     }
-    for (size_t i = 0; i < steps.size(); ++i) {
+    for (int32_t r0 = 0; slice_rows > 0 && r0 < q->S; r0 += slice_rows) {
+        // the dK/dV launches of every chunk on rows [r0, r0 + n), their dS stored one
+        // after the other, then one dQ pass over all of them
+        const int32_t n = std::min(slice_rows, q->S - r0);
+        const ra_tensor qs = seq_slice(*q, r0, n), dos = seq_slice(*dout, r0, n);
+        const ra_lse ls = rows_slice(*lse, r0, n), dls = rows_slice(delta, r0, n);
+        ra::KeyMask kms[ra::kDqsMaxChunks];
+        ra::DqsChunk more[ra::kDqsMaxChunks - 1];
+        char* dsj = (char*)ds;
+        for (size_t j = 0; j < steps.size(); ++j) {
+            const int cj = steps[j].c;
+            const int32_t st = chunks->start[cj], len = chunks->len[cj];
+            const ra_tensor kcj = seq_slice(*k, st, len), vcj = seq_slice(*v, st, len);
+            const ra_tensor dkj = seq_slice(dk_acc, st, len), dvj = seq_slice(dv_acc, st, len);
+            kms[j] = key_mask(kmask, st);
+            RA_HIP(ra::launch_bwd_dkdv_bf16(qs, kcj, vcj, dos, ls, dls, kms[j], scale, dkj, dvj, dsj, s, nullptr,
+                                            nullptr));
+            if (j > 0) more[j - 1] = ra::DqsChunk{kcj, dsj, kms[j].data ? &kms[j] : nullptr};
+            dsj += round256((size_t)ra::ds_bytes(q->B, q->H, n, len));
+        }
+        const int c0 = steps[0].c;
+        const ra_tensor k0 = seq_slice(*k, chunks->start[c0], chunks->len[c0]);
+        const ra_tensor dqs = seq_slice(dq_acc, r0, n), dqo = seq_slice(*dq, r0, n);
+        RA_HIP(ra::launch_bwd_dqs_bf16(qs, k0, ds, scale, dqs, s, false, direct_dq ? &dqo : nullptr,
+                                       kms[0].data ? &kms[0] : nullptr, more, (int)steps.size() - 1));
+    }
+    for (size_t i = 0; slice_rows == 0 && i < steps.size(); ++i) {
         const int c = steps[i].c;
         const int32_t rows = steps[i].rows;
         const ra_tensor kc = seq_slice(*k, chunks->start[c], chunks->len[c]);

@@ -271,6 +271,26 @@ def ring_bwd_workspace_bytes(q, k, dq_dtype=None, dk_dtype=None, layout="bshd", 
     return fn(tq, tk, tdq, tdk, tdk)
 
 
+def ring_bwd_plan(q, k, chunks, workspace_bytes, dq_dtype=None, dk_dtype=None, layout="bshd"):
+    """The plan ``ring_bwd`` runs with a workspace of ``workspace_bytes`` bytes (host-side,
+    no launch): a dict with ``slice_rows`` (query rows per slice when the sweep runs slice
+    by slice, else 0), ``rows`` (per chunk in sweep order: query rows per dK/dV launch on the
+    stored-dS route, 0 on the recompute route, -1 for an empty chunk) and ``accumulators``
+    (the gradients that get an fp32 accumulator in the workspace)."""
+    if not isinstance(chunks, Chunks):
+        chunks = Chunks(chunks)
+    tq, tk = tensor_desc(q, layout), tensor_desc(k, layout)
+    tdq, tdk = tensor_desc(q, layout), tensor_desc(k, layout)
+    tdq.dtype = _DT[dq_dtype or q.dtype]
+    tdk.dtype = _DT[dk_dtype or k.dtype]
+    n = chunks.c.n
+    sr, rows, accs = ctypes.c_int32(0), (ctypes.c_int32 * max(n, 1))(), ctypes.c_uint32(0)
+    check(lib().ra_ring_bwd_plan(tq, tk, tdq, tdk, tdk, ctypes.byref(chunks.c), int(workspace_bytes),
+                                 ctypes.byref(sr), rows, ctypes.byref(accs)), "ra_ring_bwd_plan")
+    return {"slice_rows": sr.value, "rows": [rows[i] for i in range(n)],
+            "accumulators": [g for b, g in ((1, "dq"), (2, "dk"), (4, "dv")) if accs.value & b]}
+
+
 def _workspace(ws, need, device):
     if need == 0:
         return None

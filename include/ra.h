@@ -244,8 +244,12 @@ ra_status ra_ring_fwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v
  * recomputing S and dP.  The sweep plans from the room ws_bytes leaves: query
  * rows go in slices (multiples of 64) when the dS of a whole chunk does not fit,
  * and a chunk whose slices would be too thin to fill the GPU takes the
- * recompute route (ra_bwd_chunk's kernels); any plan gives the same result up
- * to rounding.  fp32 accumulators for bf16 gradients are carved only where the
+ * recompute route (ra_bwd_chunk's kernels).  When the dS of every chunk does not
+ * fit at once but that of every chunk (at most 8) for a slice of 4096 or more
+ * query rows does, the sweep runs slice by slice instead: each slice runs the
+ * chunk steps of every chunk in sweep order, then one dQ pass over all of them
+ * that writes the slice's dq rows.  Any plan gives the same result up to
+ * rounding.  fp32 accumulators for bf16 gradients are carved only where the
  * plan needs them.  Results agree with ra_bwd_chunk up to rounding, not bit for
  * bit. */
 ra_status ra_ring_bwd(const ra_tensor* q, const ra_tensor* k, const ra_tensor* v,
@@ -298,6 +302,20 @@ size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k,
                                    const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);
 size_t ra_ring_bwd_workspace_min_bytes(const ra_tensor* q, const ra_tensor* k,
                                        const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);
+
+/* The plan ra_ring_bwd_masked would run for these arguments with a workspace of
+ * ws_bytes bytes, computed on the host (no launch, no device access): the same
+ * validation of q, k, the gradients (NULL: the dtype of q/k/v) and the chunk
+ * table, then *slice_rows = the query rows per slice when the sweep runs slice
+ * by slice (0: chunk by chunk); rows[i] (chunks->n entries, i-th chunk of the
+ * sweep order) = the query rows per dK/dV launch of that chunk on the stored-dS
+ * route, 0 on the recompute route, -1 for an empty chunk (or no query rows);
+ * *accs = bit 0, 1, 2 set when an fp32 accumulator for dq, dk, dv is carved from
+ * the workspace.  RA_E_WORKSPACE when ws_bytes is below what that plan needs.
+ * Any output pointer may be NULL. */
+ra_status ra_ring_bwd_plan(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq,
+                           const ra_tensor* dk, const ra_tensor* dv, const ra_chunks* chunks,
+                           size_t ws_bytes, int32_t* slice_rows, int32_t* rows, uint32_t* accs);
 
 /* ---------------------------------------------------------------- exchange */
 

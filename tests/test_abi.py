@@ -196,6 +196,58 @@ def test_ring_bwd_workspace_sizes():
     assert lib.ra_ring_bwd_workspace_bytes(bq, bk, bq, bk, bk) == r256(32 * 4096 * 4) + (8 << 30)
 
 
+def _plan(q, k, c, ws, dq=None, dk=None):
+    lib = _lib()
+    sr, rows, accs = ctypes.c_int32(-9), (ctypes.c_int32 * c.n)(), ctypes.c_uint32(99)
+    st = lib.ra_ring_bwd_plan(q, k, dq or q, dk or k, dk or k, ctypes.byref(c), ws, ctypes.byref(sr), rows,
+                              ctypes.byref(accs))
+    assert st == abi.RA_OK, lib.ra_last_error().decode()
+    return sr.value, list(rows), [g for b, g in ((1, "dq"), (2, "dk"), (4, "dv")) if accs.value & b]
+
+
+def test_ring_bwd_plans():
+    """The backward's plan for the video-DiT workload (8 chunks of 4096 keys, Hq 32 / Hkv 8,
+    D 128; 16 MiB of dS per 64 query rows and chunk) under the sizes the sweep is run with."""
+    lib = _lib()
+    r256 = lambda n: (n + 255) // 256 * 256
+    k = T(1, 32768, 8, 128)
+    c = chunks([4096] * 8, [0, 7, 6, 5, 4, 3, 2, 1])
+    shard, full = T(1, 4096, 32, 128), T(1, 32768, 32, 128)
+    acc_kv = 2 * r256(32768 * 8 * 128 * 4)
+    # rank-0 shard, recommended: the whole dS (8 GiB) in one region, one dQ pass, no accumulators
+    rec = lib.ra_ring_bwd_workspace_bytes(shard, k, shard, k, k)
+    assert _plan(shard, k, c, rec) == (0, [4096] * 8, [])
+    # ... with 2 GiB of dS room: chunk by chunk, two chunks' dS per dQ pass (fp32 dQ accumulator)
+    lo = lib.ra_ring_bwd_workspace_min_bytes(shard, k, shard, k, k)
+    assert _plan(shard, k, c, lo + (2 << 30)) == (0, [4096] * 8, ["dq"])
+    # ... with the minimum: every chunk on the recompute route
+    assert _plan(shard, k, c, lo) == (0, [0] * 8, ["dq", "dk", "dv"])
+    # full Q, recommended: 8 GiB of dS hold every chunk for 4096 rows, so the sweep runs in 8
+    # slices of 4096 rows (dQ of each slice written once; dK/dV summed over slices in fp32)
+    rec_full = lib.ra_ring_bwd_workspace_bytes(full, k, full, k, k)
+    assert rec_full == r256(32 * 32768 * 4) + acc_kv + (8 << 30)
+    assert _plan(full, k, c, rec_full) == (4096, [4096] * 8, ["dk", "dv"])
+    # ... with 2 GiB of room a slice of every chunk would be 1024 rows: chunk by chunk, each
+    # chunk in 4 slices of 8192 rows
+    lo_full = lib.ra_ring_bwd_workspace_min_bytes(full, k, full, k, k)
+    assert _plan(full, k, c, lo_full + (2 << 30)) == (0, [8192] * 8, ["dq", "dk", "dv"])
+    # fp32 gradients are their own accumulators
+    f = lambda t: T(t.B, t.S, t.H, t.D, abi.RA_F32)
+    rec32 = lib.ra_ring_bwd_workspace_bytes(full, k, f(full), f(k), f(k))
+    assert rec32 == r256(32 * 32768 * 4) + (8 << 30)
+    assert _plan(full, k, c, rec32, f(full), f(k)) == (4096, [4096] * 8, [])
+    # more room than that: longer slices (the room the unneeded accumulators leave)
+    assert _plan(full, k, c, rec_full, f(full), f(k)) == (4224, [4224] * 8, [])
+    # fp32 inputs have no dS route; an empty chunk is reported as -1
+    c3 = chunks([0, 100, 200], [2, 0, 1])
+    q32, k32 = f(T(1, 64, 4, 64)), f(T(1, 300, 2, 64))
+    assert _plan(q32, k32, c3, 1 << 20) == (0, [0, -1, 0], [])
+    # below what the plan needs
+    sr = ctypes.c_int32()
+    assert lib.ra_ring_bwd_plan(full, k, full, k, k, ctypes.byref(c), 4096, ctypes.byref(sr), None, None) == \
+        abi.RA_E_WORKSPACE
+
+
 def test_ring_bwd_refuses_below_minimum_workspace():
     lib = _lib()
     q, k, v = T(1, 100, 8, 64), T(1, 300, 2, 64), T(1, 300, 2, 64)

@@ -55,6 +55,53 @@ def test_small_workspace_plans_match_oracle():
             assert rel(np64(a), np64(b)) <= 5e-3
 
 
+@pytest.mark.parametrize("masked", [False, True], ids=["dense", "masked"])
+def test_slice_major_plan_matches_oracle(masked):
+    """A workspace whose room holds the dS of every chunk only for part of the query rows (at
+    least 4096): the sweep runs slice by slice, each slice running the chunk steps of every
+    chunk and then one dQ pass over all of them.  Ragged chunks (not multiples of a tile) and
+    a ragged last slice; with and without a key mask.  Against the oracle on every head and
+    against the plan with room for all of the dS (one dQ pass over the whole query)."""
+    d = dev()
+    B, Sq, Hq, Hkv, D = 1, 8292, 2, 1, 128
+    lens, order = [700, 1000, 300], [1, 0, 2]
+    Sk = sum(lens)
+    seed = 84 + (10 if masked else 0)
+    q = W.randn((B, Sq, Hq, D), seed, "bf16"); k = W.randn((B, Sk, Hkv, D), seed + 1, "bf16")
+    v = W.randn((B, Sk, Hkv, D), seed + 2, "bf16"); do = W.randn((B, Sq, Hq, D), seed + 3, "bf16")
+    m = W.make_key_mask(B, Sk, seed + 4, p_keep=0.8, valid_len=(1900,), masked_ranges=[(0, 100, 400)]) \
+        if masked else None
+    gq, gk, gv, gdo = (t.to(d) for t in (q, k, v, do))
+    gm = None if m is None else m.to(d)
+    ch = ra.Chunks(lens, order)
+    out, lse = ra.ring_fwd(gq, gk, gv, ch, kmask=gm)
+    starts = [sum(lens[:i]) for i in range(len(lens))]
+    room = sum(ra.bwd_ds_bytes(gq[:, :4096], gk[:, s0:s0 + n]) for s0, n in zip(starts, lens))
+    lo = ra.ring_bwd_workspace_bytes(gq, gk, minimum=True)
+    plan = ra.ring_bwd_plan(gq, gk, ch, lo + room)
+    assert 4096 <= plan["slice_rows"] < Sq and Sq % plan["slice_rows"] != 0, plan
+    assert plan["accumulators"] == ["dk", "dv"], plan
+    # room for every chunk's dS at every row: one dQ pass over the whole query (the
+    # recommended size, which sees no chunk table, counts the keys' tiles as one chunk's)
+    hi = lo + sum(ra.bwd_ds_bytes(gq, gk[:, s0:s0 + n]) for s0, n in zip(starts, lens))
+    assert ra.ring_bwd_plan(gq, gk, ch, hi) == {"slice_rows": 0, "rows": [Sq] * 3, "accumulators": []}
+
+    def run(nbytes):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
+        g = [torch.empty(t.shape, dtype=torch.bfloat16, device=d) for t in (q, k, v)]
+        ra.ring_bwd(gq, gk, gv, out, gdo, lse, ch, workspace=ws, dq=g[0], dk=g[1], dv=g[2], kmask=gm)
+        torch.cuda.synchronize()
+        return g
+
+    sliced, full = run(lo + room), run(hi)
+    mn = None if m is None else m.numpy().astype(np.uint8)
+    ref = oracle.attention_backward(np64(q), np64(k), np64(v), np64(do), kmask=mn)
+    for name, a, r in zip(("dq", "dk", "dv"), sliced, ref):
+        check_bf16(f"slice-major {name}", np64(a), r)
+    for a, b in zip(sliced, full):
+        assert rel(np64(a), np64(b)) <= 5e-3
+
+
 @pytest.mark.slow
 def test_video_shard_with_2gib_ds_budget():
     """The video-DiT shard (4096 rows, 8 chunks of 4096; 1 GiB of dS per chunk) with 2 GiB of
@@ -85,8 +132,9 @@ def test_video_shard_with_2gib_ds_budget():
 def test_full_q_with_2gib_ds_budget_slices_chunks():
     """Full Q (32768 rows; 8 GiB of dS per chunk) with 2 GiB of room for dS: every chunk is
     swept in query-row slices of 8192, the dK/dV rows of a chunk are summed over its slices
-    in fp32.  Against the run with the recommended workspace (one slice per chunk), and
-    through the key sums that hold at any size (rows of P sum to 1, rows of dS to 0)."""
+    in fp32.  Against the run with the recommended workspace (8 slices of 4096 rows, each
+    running every chunk and one dQ pass), and through the key sums that hold at any size
+    (rows of P sum to 1, rows of dS to 0)."""
     w = W.VIDEO_DIT_GQA
     lens = ra.split_sizes(w.S, w.n_chunks)
     q, k, v, do = W.make_inputs(w)

@@ -55,13 +55,16 @@ def test_small_workspace_plans_match_oracle():
             assert rel(np64(a), np64(b)) <= 5e-3
 
 
-@pytest.mark.parametrize("masked", [False, True], ids=["dense", "masked"])
-def test_slice_major_plan_matches_oracle(masked):
+@pytest.mark.parametrize("masked,grad_dtype", [(False, torch.bfloat16), (True, torch.bfloat16), (False, torch.float32)],
+                         ids=["dense", "masked", "f32_grads"])
+def test_slice_major_plan_matches_oracle(masked, grad_dtype):
     """A workspace whose room holds the dS of every chunk only for part of the query rows (at
     least 4096): the sweep runs slice by slice, each slice running the chunk steps of every
     chunk and then one dQ pass over all of them.  Ragged chunks (not multiples of a tile) and
-    a ragged last slice; with and without a key mask.  Against the oracle on every head and
-    against the plan with room for all of the dS (one dQ pass over the whole query)."""
+    a ragged last slice; with and without a key mask; bf16 gradients (dK/dV summed over the
+    slices in fp32 accumulators, dq rows written by each slice's pass) and fp32 gradients
+    (their own accumulators).  Against the oracle on every head and against the plan with
+    room for all of the dS (one dQ pass over the whole query)."""
     d = dev()
     B, Sq, Hq, Hkv, D = 1, 8292, 2, 1, 128
     lens, order = [700, 1000, 300], [1, 0, 2]
@@ -77,18 +80,19 @@ def test_slice_major_plan_matches_oracle(masked):
     out, lse = ra.ring_fwd(gq, gk, gv, ch, kmask=gm)
     starts = [sum(lens[:i]) for i in range(len(lens))]
     room = sum(ra.bwd_ds_bytes(gq[:, :4096], gk[:, s0:s0 + n]) for s0, n in zip(starts, lens))
-    lo = ra.ring_bwd_workspace_bytes(gq, gk, minimum=True)
-    plan = ra.ring_bwd_plan(gq, gk, ch, lo + room)
+    lo = ra.ring_bwd_workspace_bytes(gq, gk, grad_dtype, grad_dtype, minimum=True)
+    plan = ra.ring_bwd_plan(gq, gk, ch, lo + room, grad_dtype, grad_dtype)
     assert 4096 <= plan["slice_rows"] < Sq and Sq % plan["slice_rows"] != 0, plan
-    assert plan["accumulators"] == ["dk", "dv"], plan
+    assert plan["accumulators"] == (["dk", "dv"] if grad_dtype == torch.bfloat16 else []), plan
     # room for every chunk's dS at every row: one dQ pass over the whole query (the
     # recommended size, which sees no chunk table, counts the keys' tiles as one chunk's)
     hi = lo + sum(ra.bwd_ds_bytes(gq, gk[:, s0:s0 + n]) for s0, n in zip(starts, lens))
-    assert ra.ring_bwd_plan(gq, gk, ch, hi) == {"slice_rows": 0, "rows": [Sq] * 3, "accumulators": []}
+    assert ra.ring_bwd_plan(gq, gk, ch, hi, grad_dtype, grad_dtype) == \
+        {"slice_rows": 0, "rows": [Sq] * 3, "accumulators": []}
 
     def run(nbytes):
         ws = torch.empty(nbytes, dtype=torch.uint8, device=d)
-        g = [torch.empty(t.shape, dtype=torch.bfloat16, device=d) for t in (q, k, v)]
+        g = [torch.empty(t.shape, dtype=grad_dtype, device=d) for t in (q, k, v)]
         ra.ring_bwd(gq, gk, gv, out, gdo, lse, ch, workspace=ws, dq=g[0], dk=g[1], dv=g[2], kmask=gm)
         torch.cuda.synchronize()
         return g

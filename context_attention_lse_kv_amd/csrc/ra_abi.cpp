@@ -622,8 +622,7 @@ size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k, const
 ra_status ra_ring_bwd_plan(const ra_tensor* q, const ra_tensor* k, const ra_tensor* dq, const ra_tensor* dk,
                            const ra_tensor* dv, const ra_chunks* chunks, size_t ws_bytes, int32_t* slice_rows,
                            int32_t* rows, uint32_t* accs) {
-    RA_TRY(check_tensor(q, "q"));
-    RA_TRY(check_tensor(k, "k"));
+    RA_TRY(check_qkv(q, k, k));
     RA_TRY(check_chunks(chunks, k->S));
     const ra_tensor dq_ = dq ? *dq : *q, dk_ = dk ? *dk : *k, dv_ = dv ? *dv : *k;
     for (const ra_tensor* t : {&dq_, &dk_, &dv_})

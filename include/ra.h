@@ -304,9 +304,10 @@ size_t ra_ring_bwd_workspace_min_bytes(const ra_tensor* q, const ra_tensor* k,
                                        const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);
 
 /* The plan ra_ring_bwd_masked would run for these arguments with a workspace of
- * ws_bytes bytes, computed on the host (no launch, no device access): the same
- * validation of q, k, the gradients (NULL: the dtype of q/k/v) and the chunk
- * table, then *slice_rows = the query rows per slice when the sweep runs slice
+ * ws_bytes bytes, computed on the host (no launch, no device access): q and k
+ * validated as ra_ring_bwd validates them (k standing in for v), the gradients'
+ * dtypes (NULL: the dtype of q/k) and the chunk table; then *slice_rows = the
+ * query rows per slice when the sweep runs slice
  * by slice (0: chunk by chunk); rows[i] (chunks->n entries, i-th chunk of the
  * sweep order) = the query rows per dK/dV launch of that chunk on the stored-dS
  * route, 0 on the recompute route, -1 for an empty chunk (or no query rows);

@@ -242,8 +242,17 @@ def test_ring_bwd_plans():
     c3 = chunks([0, 100, 200], [2, 0, 1])
     q32, k32 = f(T(1, 64, 4, 64)), f(T(1, 300, 2, 64))
     assert _plan(q32, k32, c3, 1 << 20) == (0, [0, -1, 0], [])
-    # below what the plan needs
+    # refusals: a chunk table that does not tile the keys, an unknown gradient dtype, GQA
+    # heads that do not divide
     sr = ctypes.c_int32()
+    bad = chunks([4096] * 7, list(range(7)))
+    assert lib.ra_ring_bwd_plan(full, k, None, None, None, ctypes.byref(bad), rec_full, ctypes.byref(sr), None,
+                                None) == abi.RA_E_SHAPE
+    assert lib.ra_ring_bwd_plan(full, k, T(1, 32768, 32, 128, 7), None, None, ctypes.byref(c), rec_full,
+                                ctypes.byref(sr), None, None) == abi.RA_E_DTYPE
+    assert lib.ra_ring_bwd_plan(T(1, 4096, 30, 128), k, None, None, None, ctypes.byref(c), rec_full,
+                                ctypes.byref(sr), None, None) == abi.RA_E_SHAPE
+    # below what the plan needs
     assert lib.ra_ring_bwd_plan(full, k, full, k, k, ctypes.byref(c), 4096, ctypes.byref(sr), None, None) == \
         abi.RA_E_WORKSPACE
 

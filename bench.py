@@ -111,6 +111,14 @@ def run_workload(full, steps, warmup, masked=False, single=False):
                 bws=bws, step_ms=step_ms)
 
 
+def plan_record(r):
+    """The backward plan the timed sweep ran with its workspace (host-side query of the
+    library): query rows per slice when it ran slice by slice (else 0), query rows per dK/dV
+    launch of each chunk in sweep order, and the gradients given an fp32 accumulator."""
+    pl = ra.ring_bwd_plan(r["q"], r["k"], ra.Chunks(r["lens"], r["order"]), r["bws"].numel())
+    return {"workspace_bytes": int(r["bws"].numel()), **pl}
+
+
 def dominant_kernel(r, launches=8, back_to_back=True, lead_steps=3):
     """The dK/dV half of the backward chunk step as the ring backward runs it (one
     kernel launch per call: it stores the step's dS for the dQ pass and writes the
@@ -544,6 +552,7 @@ def main():
         "bwd_ms": round(r["t_bwd"] * 1e3, 4),
         "roofline": dkdv,
         "rooflines": [dkdv, fwd, dqp],
+        "bwd_plan": plan_record(r),
     }
     res["hbm_kernels"] = res_hbm
     del r
@@ -555,7 +564,8 @@ def main():
                          "tflops": round(tf / rf["t_step"] / 1e12, 2),
                          "pct_of_peak": round(100.0 * tf / rf["t_step"] / 1e12 / PEAK_BF16_TFLOPS, 2),
                          "fwd_tflops": round(rf["f_f"] / rf["t_fwd"] / 1e12, 2),
-                         "bwd_tflops": round(rf["f_b"] / rf["t_bwd"] / 1e12, 2)}
+                         "bwd_tflops": round(rf["f_b"] / rf["t_bwd"] / 1e12, 2),
+                         "bwd_plan": plan_record(rf)}
         del rf
         torch.cuda.empty_cache()
     if not args.no_masked:

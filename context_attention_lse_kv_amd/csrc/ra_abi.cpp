@@ -475,7 +475,8 @@ size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out) {
 }
 
 // dS region of the bf16 ring backward that ra_ring_bwd_workspace_bytes recommends: enough
-// for every query row against the whole key sequence, capped at kDsBudget.  The sweep
+// for every query row against every chunk of a table of up to kDqsMaxChunks chunks, capped
+// at kDsBudget.  The sweep
 // itself uses whatever room the caller's workspace leaves above the minimum: a chunk whose
 // dS does not fit is swept in query-row slices (multiples of 64 rows) that do.
 static constexpr int64_t kDsBudget = int64_t(8) << 30;
@@ -489,7 +490,11 @@ static constexpr int64_t kMinGroupRows = 4096;
 
 static size_t ds_region_bytes(const ra_tensor& q, const ra_tensor& k) {
     if (q.dtype != RA_BF16 || q.S == 0 || k.S == 0) return 0;
-    const int64_t full = ra::ds_bytes(q.B, q.H, q.S, k.S);
+    // dS is stored in whole key tiles per chunk, so a table of n chunks needs up to n - 1 key
+    // tiles more than the key sequence taken as one chunk; the room covers that for as many
+    // chunks as one dQ pass sweeps, so that any such table runs as one group
+    const int64_t full = ra::ds_bytes(q.B, q.H, q.S, k.S) +
+                         (ra::kDqsMaxChunks - 1) * ra::ds_bytes(q.B, q.H, q.S, ra::kBwdBlockN);
     return round256((size_t)(full < kDsBudget ? full : kDsBudget));
 }
 

@@ -295,8 +295,9 @@ ra_status ra_ring_fwd_noalloc(const ra_tensor* q, const ra_tensor* k, const ra_t
  * the plan it allows needs more than ws_bytes.  ra_ring_bwd_workspace_bytes: the
  * size at which ra_ring_bwd runs fastest: delta, the fp32 accumulators its plan
  * needs and a dS region of min(8 GiB, dS of every query row against the whole
- * key sequence), and never less than the minimum.  dq/dk/dv give the gradient
- * dtypes (NULL: the dtype of q/k/v). */
+ * key sequence plus 7 key tiles of 128, the rounding to whole tiles that a table
+ * of up to 8 chunks adds), and never less than the minimum.  dq/dk/dv give the
+ * gradient dtypes (NULL: the dtype of q/k/v). */
 size_t ra_ring_fwd_workspace_bytes(const ra_tensor* q, const ra_tensor* out);
 size_t ra_ring_bwd_workspace_bytes(const ra_tensor* q, const ra_tensor* k,
                                    const ra_tensor* dq, const ra_tensor* dk, const ra_tensor* dv);

@@ -170,6 +170,12 @@ def test_ring_fwd_needs_workspace_for_bf16_out():
     assert lib.ra_ring_fwd_workspace_bytes(q, T(1, 64, 8, 64, abi.RA_F32)) == 0
 
 
+def _region(lib, q, k):
+    """The recommended dS room: the whole key sequence as one chunk plus the 7 key tiles of
+    128 that splitting it into up to 8 chunks can add (each chunk's dS is whole tiles)."""
+    return lib.ra_bwd_ds_bytes(q, k) + 7 * lib.ra_bwd_ds_bytes(q, T(k.B, 128, k.H, k.D, k.dtype))
+
+
 def test_ring_bwd_workspace_sizes():
     """Recommended size: delta + the dS region (+ only the accumulators that plan needs);
     minimum: delta + an fp32 accumulator for every bf16 gradient, no dS region."""
@@ -178,7 +184,7 @@ def test_ring_bwd_workspace_sizes():
     f = lambda t: T(t.B, t.S, t.H, t.D, abi.RA_F32)
     r256 = lambda n: (n + 255) // 256 * 256
     delta = r256(8 * 100 * 4)
-    ds = lib.ra_bwd_ds_bytes(q, k)
+    ds = _region(lib, q, k)
     accs = r256(100 * 8 * 64 * 4) + 2 * r256(300 * 2 * 64 * 4)
     # fp32 gradients are their own accumulators
     assert lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k)) == delta + ds
@@ -271,8 +277,8 @@ def test_ring_bwd_refuses_below_minimum_workspace():
 
 def test_bwd_ds_bytes_and_ring_ds_region():
     """dS blocks: 4 KiB per (batch, query head, 64 query rows, 32 keys counted in whole
-    128-key tiles); the ring backward reserves min(8 GiB, that for the whole key sequence)
-    for bf16 inputs and nothing for fp32."""
+    128-key tiles); the ring backward reserves min(8 GiB, that for the whole key sequence plus
+    the tile rounding of up to 8 chunks) for bf16 inputs and nothing for fp32."""
     lib = _lib()
     q, k = T(2, 100, 8, 64), T(2, 300, 2, 64)
     assert lib.ra_bwd_ds_bytes(q, k) == 2 * 8 * 2 * (4 * 3) * 4096
@@ -283,7 +289,13 @@ def test_bwd_ds_bytes_and_ring_ds_region():
     with_ds = lib.ra_ring_bwd_workspace_bytes(q, k, f(q), f(k), f(k))
     q32, k32 = f(q), f(k)
     without = lib.ra_ring_bwd_workspace_bytes(q32, k32, q32, k32, k32)
-    assert with_ds - without == lib.ra_bwd_ds_bytes(q, k)
+    assert with_ds - without == _region(lib, q, k)
+    # the room runs any table of up to 8 chunks as one group: 300 keys as 8 ragged chunks take
+    # 8 key tiles where one chunk takes 3
+    c8 = chunks([38, 37, 38, 37, 37, 38, 37, 38], list(range(8)))
+    assert _plan(q, k, c8, with_ds, f(q), f(k)) == (0, [100] * 8, [])
+    need = sum(lib.ra_bwd_ds_bytes(q, T(2, n, 2, 64)) for n in [38, 37, 38, 37, 37, 38, 37, 38])
+    assert lib.ra_bwd_ds_bytes(q, k) < need <= _region(lib, q, k)
     big_q, big_k = T(1, 32768, 32, 128), T(1, 32768, 8, 128)
     fq, fk = f(big_q), f(big_k)
     assert lib.ra_ring_bwd_workspace_bytes(big_q, big_k, fq, fk, fk) - \

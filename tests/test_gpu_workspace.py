@@ -42,6 +42,9 @@ def test_small_workspace_plans_match_oracle():
     hi = ra.ring_bwd_workspace_bytes(gq, gk)
     one_chunk_ds = ra.bwd_ds_bytes(gq, gk[:, :200])
     assert lo < hi
+    assert ra.ring_bwd_plan(gq, gk, ch, hi) == {"slice_rows": 0, "rows": [200] * 3, "accumulators": []}
+    assert ra.ring_bwd_plan(gq, gk, ch, lo + one_chunk_ds + 4096) == \
+        {"slice_rows": 0, "rows": [200] * 3, "accumulators": ["dq"]}
     results = {}
     # minimum: every chunk on the recompute route; + one chunk's dS: one chunk per dQ pass
     # (fp32 dQ accumulator, bf16 dK/dV direct); recommended: one dQ pass for all three

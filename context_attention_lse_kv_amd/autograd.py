@@ -39,57 +39,71 @@ def _dims(q, layout):
 # ------------------------------------------------------------------ attention
 @torch.library.custom_op("ra::ring_attn_fwd", mutates_args=())
 def _ring_attn_fwd(q: Tensor, k: Tensor, v: Tensor, lens: List[int], order: List[int], scale: float,
-                   kmask: Optional[Tensor], layout: str) -> Tuple[Tensor, Tensor]:
+                   kmask: Optional[Tensor], layout: str, bwd_ws: int) -> Tuple[Tensor, Tensor]:
     out, lse = ops.ring_fwd(q, k, v, ops.Chunks(lens, order), scale=scale, layout=layout, kmask=kmask)
     return out, lse
 
 
 @_ring_attn_fwd.register_fake
-def _ring_attn_fwd_fake(q, k, v, lens, order, scale, kmask, layout):
+def _ring_attn_fwd_fake(q, k, v, lens, order, scale, kmask, layout, bwd_ws):
     B, Sq, H = _dims(q, layout)
     return q.new_empty(q.shape), q.new_empty((B, H, Sq), dtype=torch.float32)
 
 
 @torch.library.custom_op("ra::ring_attn_bwd", mutates_args=())
 def _ring_attn_bwd(q: Tensor, k: Tensor, v: Tensor, out: Tensor, dout: Tensor, lse: Tensor, lens: List[int],
-                   order: List[int], scale: float, kmask: Optional[Tensor],
-                   layout: str) -> Tuple[Tensor, Tensor, Tensor]:
+                   order: List[int], scale: float, kmask: Optional[Tensor], layout: str,
+                   bwd_ws: int) -> Tuple[Tensor, Tensor, Tensor]:
+    ws = None
+    if bwd_ws > 0:
+        # a cap on the backward's workspace: the library plans its sweep from the room it gets
+        # (never below the size it accepts with any chunk table)
+        lo = ops.ring_bwd_workspace_bytes(q, k, layout=layout, minimum=True)
+        hi = ops.ring_bwd_workspace_bytes(q, k, layout=layout)
+        n = max(lo, min(hi, int(bwd_ws)))
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)[:n] if n else None
     dq, dk, dv = ops.ring_bwd(q, k, v, out, dout, lse, ops.Chunks(lens, order), scale=scale, layout=layout,
-                              kmask=kmask)
+                              kmask=kmask, workspace=ws)
     return dq, dk, dv
 
 
 @_ring_attn_bwd.register_fake
-def _ring_attn_bwd_fake(q, k, v, out, dout, lse, lens, order, scale, kmask, layout):
+def _ring_attn_bwd_fake(q, k, v, out, dout, lse, lens, order, scale, kmask, layout, bwd_ws):
     return q.new_empty(q.shape), k.new_empty(k.shape), v.new_empty(v.shape)
 
 
 def _ring_attn_setup(ctx, inputs, output):
-    q, k, v, lens, order, scale, kmask, layout = inputs
+    q, k, v, lens, order, scale, kmask, layout, bwd_ws = inputs
     out, lse = output
     ctx.save_for_backward(q, k, v, out, lse, kmask)
-    ctx.args = (list(lens), list(order), float(scale), layout)
+    ctx.args = (list(lens), list(order), float(scale), layout, int(bwd_ws))
     ctx.mark_non_differentiable(lse)
 
 
 def _ring_attn_backward(ctx, grad_out, grad_lse):
     q, k, v, out, lse, kmask = ctx.saved_tensors
-    lens, order, scale, layout = ctx.args
+    lens, order, scale, layout, bwd_ws = ctx.args
     # the kernels need D contiguous; an incoming gradient may be a broadcast view
-    dq, dk, dv = _ring_attn_bwd(q, k, v, out, grad_out.contiguous(), lse, lens, order, scale, kmask, layout)
-    return dq, dk, dv, None, None, None, None, None
+    dq, dk, dv = _ring_attn_bwd(q, k, v, out, grad_out.contiguous(), lse, lens, order, scale, kmask, layout,
+                                bwd_ws)
+    return dq, dk, dv, None, None, None, None, None, None
 
 
 torch.library.register_autograd("ra::ring_attn_fwd", _ring_attn_backward, setup_context=_ring_attn_setup)
 
 
-def ring_attention(q, k, v, chunks, scale=None, kmask=None, layout="bshd", return_lse=False):
+def ring_attention(q, k, v, chunks, scale=None, kmask=None, layout="bshd", return_lse=False,
+                   bwd_workspace_bytes=0):
     """Ring attention of the query shard ``q`` over the chunks of (k, v), differentiable
     in q, k, v (backward: one chunk step per forward step, each against its own chunk).
 
     ``chunks``: an ``ops.Chunks`` or a list of chunk lengths (swept in order).  A single
     chunk covering the whole key sequence is the all-gather variant: one fused sweep
     with no per-step merge.  ``kmask``: optional key-validity mask [B, S_k].
+    ``bwd_workspace_bytes``: a cap on the device workspace the backward allocates (0: the
+    size at which it runs fastest, up to 8 GiB of stored dS); with less room the backward
+    groups fewer chunks per dQ pass, sweeps query-row slices or recomputes, with the same
+    result up to rounding.  Never below the minimum the library accepts.
     """
     # plain lists only here (no ctypes objects), so that a compiled graph traces through
     if isinstance(chunks, ops.Chunks):
@@ -98,7 +112,7 @@ def ring_attention(q, k, v, chunks, scale=None, kmask=None, layout="bshd", retur
         lens = [int(n) for n in chunks]
         order = list(range(len(lens)))
     sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
-    out, lse = _ring_attn_fwd(q, k, v, lens, order, sc, kmask, layout)
+    out, lse = _ring_attn_fwd(q, k, v, lens, order, sc, kmask, layout, int(bwd_workspace_bytes))
     return (out, lse) if return_lse else out
 
 

@@ -55,6 +55,31 @@ def test_autograd_matches_ring_bwd_and_oracle():
         check_bf16('grad', np64(a), b)
 
 
+def test_autograd_backward_workspace_cap():
+    """``bwd_workspace_bytes`` caps the backward's workspace: at the minimum every chunk takes
+    the recompute route, with room for one chunk's dS the chunks run one dQ pass each; both
+    give the gradients of the uncapped backward up to rounding, and the oracle's."""
+    B, S, Sq, Hq, Hkv, D = 2, 600, 200, 8, 2, 64
+    q, k, v, do = (W.randn(s, 1120 + i, "bf16") for i, s in enumerate([(B, Sq, Hq, D), (B, S, Hkv, D),
+                                                                        (B, S, Hkv, D), (B, Sq, Hq, D)]))
+    ch = ra.Chunks((200, 200, 200), (1, 0, 2))
+    gdo = do.to(dev()).float()
+    gq, gk = q.to(dev()), k.to(dev())
+    lo = ra.ring_bwd_workspace_bytes(gq, gk, minimum=True)
+    one = lo + ra.bwd_ds_bytes(gq, gk[:, :200]) + 4096
+    assert ra.ring_bwd_plan(gq, gk, ch, lo)["rows"] == [0, 0, 0]
+    assert ra.ring_bwd_plan(gq, gk, ch, one)["accumulators"] == ["dq"]
+    _, full = _grads(lambda a, b, c: ra.ring_attention(a, b, c, ch), _leaves(q, k, v), gdo)
+    qn, kn, vn, don = (np64(t) for t in (q, k, v, do))
+    g = oracle.attention_backward(qn, kn, vn, don)
+    for cap in (1, one):
+        _, capped = _grads(lambda a, b, c: ra.ring_attention(a, b, c, ch, bwd_workspace_bytes=cap),
+                           _leaves(q, k, v), gdo)
+        for a, b, r in zip(capped, full, g):
+            assert rel(np64(a), np64(b)) <= 5e-3
+            check_bf16(f"grad (cap {cap})", np64(a), r)
+
+
 @pytest.mark.parametrize("masked", [False, True])
 def test_compiled_equals_eager(masked):
     B, S, Sq, Hq, Hkv, D = 2, 384, 192, 4, 2, 64
